@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for GQA decode and prefill.
+
+This module serves both the GPU library's tests/benchmark and the CPU oracle.
+It holds no attention arithmetic: only random draws, the rounding of those
+draws to bf16, and the workload shapes.
+
+Recipe (stable across runs, thread counts and machines):
+
+* every tensor is drawn from numpy's PCG64 ``default_rng`` seeded with a list
+  of integers ``[seed, tag]`` (q) or ``[seed, tag, b]`` (one stream per
+  sequence b for K and V, and per sequence for prefill Q), with tags
+  q=1, K=2, V=3; ragged lengths come from ``[seed, 0]``;
+* values are ``standard_normal(dtype=float32)``, i.e. N(0, 1);
+* bf16 tensors are the float32 draws rounded to nearest-even by integer bit
+  arithmetic, stored as uint16 bit patterns;
+* cache rows at or beyond ``seqlens[b]`` are never drawn: they hold NaN
+  (``invalid="nan"``, parity runs, proving they are never read) or zero
+  (``invalid="zero"``).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TAG_LEN, TAG_Q, TAG_K, TAG_V = 0, 1, 2, 3
+NAN_BF16 = np.uint16(0x7FC0)
+NAN_F32_BITS = np.uint32(0x7FC00000)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bit patterns.
+
+    Inputs here are finite draws, so no NaN/Inf handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def _draw(seed_words, shape, dtype: str) -> np.ndarray:
+    rng = np.random.default_rng(list(seed_words))
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return bf16_bits_from_f32(x)
+    raise ValueError(dtype)
+
+
+def _storage(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def _fill_invalid(arr: np.ndarray, dtype: str, invalid: str) -> None:
+    if invalid == "zero":
+        arr[...] = 0
+    elif invalid == "nan":
+        if dtype == "f32":
+            arr.view(np.uint32)[...] = NAN_F32_BITS
+        else:
+            arr[...] = NAN_BF16
+    else:
+        raise ValueError(invalid)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+@dataclass
+class DecodeCase:
+    name: str
+    q: np.ndarray          # [B, Hq, d]
+    k: np.ndarray          # [B, Lmax, Hkv, d]
+    v: np.ndarray          # [B, Lmax, Hkv, d]
+    seqlens: np.ndarray    # [B] int32
+    scale: float
+    dtype: str             # "f32" or "bf16"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        B, Hq, d = self.q.shape
+        return dict(B=B, Hq=Hq, Hkv=self.k.shape[2], d=d, Lmax=self.k.shape[1])
+
+
+@dataclass
+class PrefillCase:
+    name: str
+    q: np.ndarray          # [B, P, Hq, d]
+    k: np.ndarray          # [B, P, Hkv, d]
+    v: np.ndarray          # [B, P, Hkv, d]
+    causal: bool
+    scale: float
+    dtype: str
+    meta: dict = field(default_factory=dict)
+
+
+def decode_case(B, Hq, Hkv, d, Lmax, seqlens, dtype, q_seed, kv_seed, invalid="nan",
+                scale=None, name="decode") -> DecodeCase:
+    """q from [q_seed, 1]; K[b], V[b] rows < seqlens[b] from [kv_seed, 2|3, b]."""
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    assert seqlens.shape == (B,)
+    st = _storage(dtype)
+    q = _draw([q_seed, TAG_Q], (B, Hq, d), dtype)
+    k = np.empty((B, Lmax, Hkv, d), st)
+    v = np.empty((B, Lmax, Hkv, d), st)
+
+    def one(b):
+        n = int(seqlens[b])
+        k[b, :n] = _draw([kv_seed, TAG_K, b], (n, Hkv, d), dtype)
+        v[b, :n] = _draw([kv_seed, TAG_V, b], (n, Hkv, d), dtype)
+        if n < Lmax:
+            _fill_invalid(k[b, n:], dtype, invalid)
+            _fill_invalid(v[b, n:], dtype, invalid)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(B)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return DecodeCase(name, q, k, v, seqlens, float(scale), dtype,
+                      dict(q_seed=q_seed, kv_seed=kv_seed, invalid=invalid))
+
+
+def prefill_case(B, P, Hq, Hkv, d, dtype, seed, causal=True, scale=None,
+                 name="prefill") -> PrefillCase:
+    """Q[b], K[b], V[b] from [seed, 1|2|3, b]."""
+    st = _storage(dtype)
+    q = np.empty((B, P, Hq, d), st)
+    k = np.empty((B, P, Hkv, d), st)
+    v = np.empty((B, P, Hkv, d), st)
+
+    def one(b):
+        q[b] = _draw([seed, TAG_Q, b], (P, Hq, d), dtype)
+        k[b] = _draw([seed, TAG_K, b], (P, Hkv, d), dtype)
+        v[b] = _draw([seed, TAG_V, b], (P, Hkv, d), dtype)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(B)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return PrefillCase(name, q, k, v, bool(causal), float(scale), dtype, dict(seed=seed))
+
+
+# --------------------------------------------------------------------------
+# The five workloads.
+# --------------------------------------------------------------------------
+
+def tiny_decode(hkv: int, invalid="nan") -> DecodeCase:
+    """fp32, B=1, Hq=8, d=64, L=128; the same q for every hkv (2 = GQA, 8 = MHA, 1 = MQA)."""
+    return decode_case(1, 8, hkv, 64, 128, [128], "f32", q_seed=1, kv_seed=10 + hkv,
+                       invalid=invalid, name="tiny_fp32_B1_Hq8_Hkv%d_d64_L128" % hkv)
+
+
+def decode_70b(invalid="zero") -> DecodeCase:
+    """70B-class layer decode: bf16, B=32, Hq=64, Hkv=8, d=128, every sequence at L=4096."""
+    return decode_case(32, 64, 8, 128, 4096, [4096] * 32, "bf16", q_seed=2, kv_seed=2,
+                       invalid=invalid, name="decode_bf16_B32_Hq64_Hkv8_d128_L4096")
+
+
+SWEEP_HKV = (64, 16, 8, 4, 1)
+
+
+def sweep_decode(hkv: int, invalid="zero") -> DecodeCase:
+    """Head-sharing sweep: bf16, B=16, Hq=64, d=128, L=2048; one q for every hkv."""
+    return decode_case(16, 64, hkv, 128, 2048, [2048] * 16, "bf16", q_seed=3, kv_seed=30 + hkv,
+                       invalid=invalid, name="sweep_bf16_B16_Hq64_Hkv%d_d128_L2048" % hkv)
+
+
+def ragged_seqlens(B=64, Lmax=32768, seed=4) -> np.ndarray:
+    rng = np.random.default_rng([seed, TAG_LEN])
+    return rng.integers(1, Lmax + 1, B).astype(np.int32)
+
+
+def ragged_decode(invalid="nan") -> DecodeCase:
+    """Ragged batch: bf16, B=64, Hq=32, Hkv=8, d=128, Lmax=32768, seqlens ~ U[1, 32768]."""
+    sl = ragged_seqlens()
+    return decode_case(64, 32, 8, 128, 32768, sl, "bf16", q_seed=4, kv_seed=4, invalid=invalid,
+                       name="ragged_bf16_B64_Hq32_Hkv8_d128_Lmax32768")
+
+
+def prefill_causal() -> PrefillCase:
+    """Causal prefill: bf16, B=2, P=4096, Hq=32, Hkv=8, d=128."""
+    return prefill_case(2, 4096, 32, 8, 128, "bf16", seed=5, causal=True,
+                        name="prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal")

@@ -1,0 +1,361 @@
+/*
+ * gqa_oracle.c -- plain, slow, fp64 CPU reference for grouped-query attention
+ * (GQA) over a KV cache.
+ *
+ * TEST INFRASTRUCTURE.  Nothing in the product library calls, links or
+ * includes this file.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header or constant
+ * with the HIP path.
+ *
+ * What it computes (sources are the pages' titles and sections):
+ *   - "GQA reading notes" (zhongzhuzhou.org), section "方法详解 > GQA 架构":
+ *     query head h (1-indexed) belongs to group g(h) = ceil(h / (H/G)) and
+ *     head_h = softmax(Q_h K_g(h)^T / sqrt(d_k)) V_g(h).  With 0-indexed heads
+ *     that is g = floor(h / (H/G)): contiguous blocks of H/G query heads share
+ *     one K/V head.
+ *   - Same page, Algorithm 2 (GQA decode, step t), the per-query-head part:
+ *     scores over every cached row of group g, softmax, weighted sum of V.
+ *     Appending the new token's K/V happens before this call (the caller's
+ *     seqlens[b] already counts it).
+ *   - "从MHA到GQA" (gzher.com), section on why the question becomes how KV is
+ *     stored: prefill attends every prompt position under a causal mask;
+ *     decode attends one new query to all cached rows.
+ *
+ * Arithmetic: every input element is converted exactly to double (fp32 and
+ * bf16 both widen exactly), all sums run in double in a fixed ascending
+ * order, exp() is the C library's, and the softmax subtracts the row maximum
+ * before exponentiating (equal to the plain softmax in exact arithmetic).
+ *
+ * Layouts (row-major, contiguous):
+ *   decode : q [B,Hq,d]; k, v [B,Lmax,Hkv,d]; seqlens [B] (int32); out [rows,d]
+ *   prefill: q [B,P,Hq,d]; k, v [B,P,Hkv,d]; out [rows,d]
+ * dtype 0 = fp32 values, 1 = bf16 bit patterns (uint16).
+ *
+ * A row with zero valid keys (seqlens[b] == 0) is defined to be all zeros.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Exact widening of one stored element to double. */
+static double orc_elem(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Attention of one query row over n key/value rows.
+ *   qrow   : element offset of the query row in q
+ *   kv0    : element offset of key/value row 0 in k and v
+ *   stride : element distance between consecutive key rows
+ * w (length >= n) and acc (length >= d) are scratch.  Writes d values to out
+ * and, if wout is not NULL, the normalised weights w_j / Z to wout.
+ */
+static void orc_attend(const void *q, int64_t qrow, const void *k, const void *v,
+                       int64_t kv0, int64_t stride, int64_t n, int64_t d,
+                       double scale, int dtype, double *w, double *acc,
+                       double *out, double *wout)
+{
+    if (n <= 0) {
+        for (int64_t c = 0; c < d; ++c)
+            out[c] = 0.0;
+        return;
+    }
+    /* scores s_j = scale * (q . k_j), dot product summed over c ascending */
+    for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        const int64_t kr = kv0 + j * stride;
+        for (int64_t c = 0; c < d; ++c)
+            dot += orc_elem(q, qrow + c, dtype) * orc_elem(k, kr + c, dtype);
+        w[j] = dot * scale;
+    }
+    /* softmax over j: subtract the maximum, exponentiate, sum j ascending */
+    double m = w[0];
+    for (int64_t j = 1; j < n; ++j)
+        if (w[j] > m)
+            m = w[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        w[j] = exp(w[j] - m);
+        z += w[j];
+    }
+    /* out_c = (sum_j w_j * v_jc) / Z, j ascending for every c */
+    for (int64_t c = 0; c < d; ++c)
+        acc[c] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        const int64_t vr = kv0 + j * stride;
+        for (int64_t c = 0; c < d; ++c)
+            acc[c] += w[j] * orc_elem(v, vr + c, dtype);
+    }
+    for (int64_t c = 0; c < d; ++c)
+        out[c] = acc[c] / z;
+    if (wout)
+        for (int64_t j = 0; j < n; ++j)
+            wout[j] = w[j] / z;
+}
+
+static int orc_check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int dtype)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+        return -1;
+    if (Hq % Hkv != 0)
+        return -2; /* H must be divisible by the number of groups */
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -3;
+    return 0;
+}
+
+/*
+ * Decode: one new query per sequence against that sequence's cached rows.
+ * rows == NULL computes all B*Hq rows in order (nrows must be B*Hq);
+ * otherwise rows[i] = b*Hq + h selects which (b, h) rows to compute.
+ * Returns 0, or a negative code for invalid arguments.
+ */
+int oracle_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t Lmax,
+                  double scale, int dtype, const int64_t *rows, int64_t nrows,
+                  double *out)
+{
+    int rc = orc_check_common(B, Hq, Hkv, d, dtype);
+    if (rc)
+        return rc;
+    if (Lmax < 0)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] > Lmax)
+            return -4;
+    if (!rows && nrows != B * Hq)
+        return -5;
+    const int64_t gsize = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!w || !acc) {
+#pragma omp atomic write
+            err = -6;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < nrows; ++i) {
+                const int64_t r = rows ? rows[i] : i;
+                if (r < 0 || r >= B * Hq) {
+#pragma omp atomic write
+                    err = -5;
+                    continue;
+                }
+                const int64_t b = r / Hq, h = r % Hq;
+                const int64_t g = h / gsize; /* contiguous groups */
+                const int64_t n = seqlens[b];
+                orc_attend(q, (b * Hq + h) * d, k, v, ((b * Lmax) * Hkv + g) * d,
+                           Hkv * d, n, d, scale, dtype, w, acc, out + i * d, NULL);
+            }
+        }
+        free(w);
+        free(acc);
+    }
+    return err;
+}
+
+/* Normalised softmax weights of decode row (b, h): wout[j], j < seqlens[b]. */
+int oracle_decode_weights(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t Lmax,
+                          double scale, int dtype, int64_t b, int64_t h, double *wout,
+                          double *out)
+{
+    int rc = orc_check_common(B, Hq, Hkv, d, dtype);
+    if (rc)
+        return rc;
+    if (b < 0 || b >= B || h < 0 || h >= Hq || seqlens[b] < 0 || seqlens[b] > Lmax)
+        return -4;
+    const int64_t g = h / (Hq / Hkv);
+    const int64_t n = seqlens[b];
+    double *w = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!w || !acc) {
+        free(w);
+        free(acc);
+        return -6;
+    }
+    orc_attend(q, (b * Hq + h) * d, k, v, ((b * Lmax) * Hkv + g) * d, Hkv * d, n, d,
+               scale, dtype, w, acc, out, wout);
+    free(w);
+    free(acc);
+    return 0;
+}
+
+/*
+ * Prefill: every prompt position i of every sequence attends to keys
+ * j in [0, i] (causal) or [0, P) (not causal).  rows == NULL computes all
+ * B*P*Hq rows; otherwise rows[i] = (b*P + pos)*Hq + h.
+ */
+int oracle_prefill(const void *q, const void *k, const void *v, int64_t B, int64_t P,
+                   int64_t Hq, int64_t Hkv, int64_t d, int causal, double scale, int dtype,
+                   const int64_t *rows, int64_t nrows, double *out)
+{
+    int rc = orc_check_common(B, Hq, Hkv, d, dtype);
+    if (rc)
+        return rc;
+    if (P < 0)
+        return -1;
+    if (!rows && nrows != B * P * Hq)
+        return -5;
+    const int64_t gsize = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!w || !acc) {
+#pragma omp atomic write
+            err = -6;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < nrows; ++i) {
+                const int64_t r = rows ? rows[i] : i;
+                if (r < 0 || r >= B * P * Hq) {
+#pragma omp atomic write
+                    err = -5;
+                    continue;
+                }
+                const int64_t h = r % Hq, bp = r / Hq;
+                const int64_t b = bp / P, pos = bp % P;
+                const int64_t g = h / gsize;
+                const int64_t n = causal ? pos + 1 : P;
+                orc_attend(q, (bp * Hq + h) * d, k, v, ((b * P) * Hkv + g) * d, Hkv * d, n, d,
+                           scale, dtype, w, acc, out + i * d, NULL);
+            }
+        }
+        free(w);
+        free(acc);
+    }
+    return err;
+}
+
+/*
+ * Multi-head attention decode, written on its own: every query head h reads
+ * its own K/V head h (k, v are [B,Lmax,H,d]).  No group index anywhere.
+ * Same operation order as oracle_decode.
+ */
+int oracle_mha_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                      int64_t B, int64_t H, int64_t d, int64_t Lmax, double scale, int dtype,
+                      double *out)
+{
+    if (B < 0 || H <= 0 || d <= 0 || Lmax < 0 || (dtype != ORC_F32 && dtype != ORC_BF16))
+        return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t n = seqlens[b];
+        if (n < 0 || n > Lmax)
+            return -4;
+        for (int64_t h = 0; h < H; ++h) {
+            double *o = out + (b * H + h) * d;
+            if (n == 0) {
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] = 0.0;
+                continue;
+            }
+            double *s = (double *)malloc(sizeof(double) * (size_t)n);
+            if (!s)
+                return -6;
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += orc_elem(q, (b * H + h) * d + c, dtype) *
+                           orc_elem(k, ((b * Lmax + j) * H + h) * d + c, dtype);
+                s[j] = dot * scale;
+            }
+            double m = s[0];
+            for (int64_t j = 1; j < n; ++j)
+                if (s[j] > m)
+                    m = s[j];
+            double z = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                s[j] = exp(s[j] - m);
+                z += s[j];
+            }
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += s[j] * orc_elem(v, ((b * Lmax + j) * H + h) * d + c, dtype);
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = o[c] / z;
+            free(s);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Multi-query attention decode, written on its own: all H query heads read
+ * the single K/V head (k, v are [B,Lmax,1,d]).  Same operation order.
+ */
+int oracle_mqa_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                      int64_t B, int64_t H, int64_t d, int64_t Lmax, double scale, int dtype,
+                      double *out)
+{
+    if (B < 0 || H <= 0 || d <= 0 || Lmax < 0 || (dtype != ORC_F32 && dtype != ORC_BF16))
+        return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t n = seqlens[b];
+        if (n < 0 || n > Lmax)
+            return -4;
+        for (int64_t h = 0; h < H; ++h) {
+            double *o = out + (b * H + h) * d;
+            if (n == 0) {
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] = 0.0;
+                continue;
+            }
+            double *s = (double *)malloc(sizeof(double) * (size_t)n);
+            if (!s)
+                return -6;
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += orc_elem(q, (b * H + h) * d + c, dtype) *
+                           orc_elem(k, (b * Lmax + j) * d + c, dtype);
+                s[j] = dot * scale;
+            }
+            double m = s[0];
+            for (int64_t j = 1; j < n; ++j)
+                if (s[j] > m)
+                    m = s[j];
+            double z = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                s[j] = exp(s[j] - m);
+                z += s[j];
+            }
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += s[j] * orc_elem(v, (b * Lmax + j) * d + c, dtype);
+            for (int64_t c = 0; c < d; ++c)
+                o[c] = o[c] / z;
+            free(s);
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,202 @@
+"""ctypes front end of the fp64 C oracle (``gqa_oracle.c``).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's CPU
+baseline use this module.  The product library never imports it.
+
+Inputs are numpy arrays exactly as the GPU receives them: float32 values, or
+bf16 bit patterns stored as uint16.  The C code widens every element exactly
+to double and returns double results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gqa_oracle.c into liboracle.so with gcc (fp64, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    i64, vp, dbl, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, dbl, ci, vp, i64, vp]
+    lib.oracle_decode.restype = ci
+    lib.oracle_decode_weights.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, dbl, ci,
+                                          i64, i64, vp, vp]
+    lib.oracle_decode_weights.restype = ci
+    lib.oracle_prefill.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ci, dbl, ci, vp, i64, vp]
+    lib.oracle_prefill.restype = ci
+    lib.oracle_mha_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, dbl, ci, vp]
+    lib.oracle_mha_decode.restype = ci
+    lib.oracle_mqa_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, dbl, ci, vp]
+    lib.oracle_mqa_decode.restype = ci
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ci
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def swap_library(path):
+    """Point this module at another build of the oracle (used by the mutation
+    tests, which compile deliberately broken copies); returns the previous
+    handle, or None.  Pass None to restore the default on next use."""
+    global _lib
+    prev = _lib
+    _lib = None if path is None else _bind(ctypes.CDLL(path))
+    return prev
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 values or uint16 bf16 bit patterns, got %s" % a.dtype)
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("oracle inputs must be C-contiguous")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on (OMP_NUM_THREADS or all cores)."""
+    return _load().oracle_num_threads()
+
+
+def decode(q, k, v, seqlens, scale, rows=None) -> np.ndarray:
+    """GQA decode.  q [B,Hq,d]; k, v [B,Lmax,Hkv,d]; seqlens [B] int.
+
+    Returns [B,Hq,d] float64, or [len(rows),d] when ``rows`` (flat b*Hq+h
+    indices) is given.
+    """
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    B, Hq, d = q.shape
+    Bk, Lmax, Hkv, dk = k.shape
+    assert Bk == B and dk == d and v.shape == k.shape
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    assert sl.shape == (B,)
+    if rows is None:
+        out = np.empty((B, Hq, d), np.float64)
+        r, nrows = None, B * Hq
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((r.size, d), np.float64)
+        nrows = r.size
+    rc = _load().oracle_decode(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
+                               B, Hq, Hkv, d, Lmax, float(scale), dt, _ptr(r), nrows,
+                               out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_decode returned %d" % rc)
+    return out
+
+
+def decode_weights(q, k, v, seqlens, scale, b, h):
+    """(weights[seqlens[b]], out[d]) of decode row (b, h); weights are normalised."""
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    _, Lmax, Hkv, _ = k.shape
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    w = np.empty(max(int(sl[b]), 1), np.float64)
+    out = np.empty(d, np.float64)
+    rc = _load().oracle_decode_weights(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                       sl.ctypes.data, B, Hq, Hkv, d, Lmax, float(scale), dt,
+                                       int(b), int(h), w.ctypes.data, out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_decode_weights returned %d" % rc)
+    return w[: int(sl[b])], out
+
+
+def prefill(q, k, v, causal, scale, rows=None) -> np.ndarray:
+    """GQA prefill.  q [B,P,Hq,d]; k, v [B,P,Hkv,d].
+
+    Returns [B,P,Hq,d] float64, or [len(rows),d] for flat (b*P+i)*Hq+h rows.
+    """
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    B, P, Hq, d = q.shape
+    Bk, Pk, Hkv, dk = k.shape
+    assert (Bk, Pk, dk) == (B, P, d) and v.shape == k.shape
+    if rows is None:
+        out = np.empty((B, P, Hq, d), np.float64)
+        r, nrows = None, B * P * Hq
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((r.size, d), np.float64)
+        nrows = r.size
+    rc = _load().oracle_prefill(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, P, Hq, Hkv, d,
+                                1 if causal else 0, float(scale), dt, _ptr(r), nrows,
+                                out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_prefill returned %d" % rc)
+    return out
+
+
+def mha_decode(q, k, v, seqlens, scale) -> np.ndarray:
+    """Multi-head attention decode (k, v have exactly Hq heads)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    B, H, d = q.shape
+    assert k.shape[2] == H and k.shape[3] == d
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    out = np.empty((B, H, d), np.float64)
+    rc = _load().oracle_mha_decode(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
+                                   B, H, d, k.shape[1], float(scale), dt, out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_mha_decode returned %d" % rc)
+    return out
+
+
+def mqa_decode(q, k, v, seqlens, scale) -> np.ndarray:
+    """Multi-query attention decode (k, v have exactly one head)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    B, H, d = q.shape
+    assert k.shape[2] == 1 and k.shape[3] == d
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    out = np.empty((B, H, d), np.float64)
+    rc = _load().oracle_mqa_decode(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
+                                   B, H, d, k.shape[1], float(scale), dt, out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_mqa_decode returned %d" % rc)
+    return out
