@@ -1,0 +1,13 @@
+"""Grouped-query attention over a KV cache on AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libgqa.so`` (hand-written HIP kernels behind the
+C ABI of ``include/gqa.h``); this package is its Python binding.
+
+* ``decode(q, k_cache, v_cache, seqlens)`` -- one new token per sequence.
+* ``prefill(q, k, v, causal=True)`` -- the whole prompt at once.
+* count helpers: ``kv_cache_elems``, ``decode_bytes``, ``decode_flops``,
+  ``prefill_flops``, ``prefill_bytes``.
+"""
+from ._native import (BF16, EXPORTS, F32, LIBRARY_PATH, GqaError, Status, decode,  # noqa: F401
+                      decode_bytes, decode_flops, decode_num_splits, decode_workspace_size,
+                      kv_cache_elems, load, prefill, prefill_bytes, prefill_flops, status_str)

@@ -1,0 +1,437 @@
+// GQA decode kernels for gfx950.
+//
+// One workgroup per (sequence b, KV head g, split s) streams rows
+// [s*chunk, min((s+1)*chunk, seqlens[b])) of K and V for head g once and
+// serves every query head of the group from them ("GQA reading notes",
+// zhongzhuzhou.org, walkthrough of Algorithm 2: fuse the group's queries so
+// each cached K vector is read once).  Each split keeps a running maximum m,
+// a running sum of weights l and an unnormalised weighted sum acc (online
+// softmax).  With one split the workgroup writes the output; otherwise it
+// writes (m, l, acc) to the workspace and decode_merge combines the splits
+// (the long sequence cut into blocks computed independently and then fused:
+// "GQA注意力机制" article, intelliparadigm.com, section 4.2).
+//
+// Softmax runs in base 2: scores are multiplied by scale*log2(e) and the
+// weights are 2^(s - m), equal to e^(scale*dot - max) in exact arithmetic.
+#pragma once
+
+#include "common.hpp"
+
+namespace gqa {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kDecodeStep = 32;  // keys one wave consumes per step (bf16 kernel)
+
+template <int D> struct VFragT;
+template <> struct VFragT<128> { typedef u32x4 T; };
+template <> struct VFragT<64> { typedef u32x2 T; };
+
+template <int D>
+__device__ __forceinline__ typename VFragT<D>::T load_vfrag(const uint16_t* p, bool ok) {
+    typedef typename VFragT<D>::T T;
+    T z{};
+    if (ok) z = *reinterpret_cast<const T*>(p);
+    return z;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 split kernel on the matrix cores.
+//
+// Per wave and step of 32 keys (two 16-key sub-tiles t):
+//   scores  S^T[key][head] = K Q^T with v_mfma_f32_16x16x32_bf16: A = K rows
+//           (lane: key 16t + lane%16, 8 head-dim values), B = the group's
+//           queries (lane: head lane%16, same 8 head-dim values); the 16
+//           MFMA columns are up to 16 query heads of the group, so one K
+//           fragment serves them all.  Products of bf16 values are exact in
+//           fp32 and the sum is fp32.
+//   result  lane holds the scores of keys 16t + 4*(lane/16) + r (r < 4) for
+//           head lane%16 -- exactly the A-operand layout of the P*V product.
+//   P*V     O[head][dim] += P[head][key] V[key][dim], again 16x16x32 MFMA;
+//           V fragments are 8 keys x 1 head-dim value per lane, built from
+//           row loads (lane: 8 consecutive head-dim values of one key) with
+//           byte permutes.  P is fed as two bf16 terms, hi = truncation of p
+//           and lo = p - hi rounded, so the weights carry ~16 significant
+//           bits and the accumulation is fp32.
+// NT = number of 16-head tiles (ceil(group size / 16)).
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ seqlens, int Hq, int Hkv,
+    int Lmax, int gsize, int S, int chunk, float c_log2, uint16_t* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    constexpr int KI = D / 32;   // 32-wide slices of the head dim
+    constexpr int EPL = D / 16;  // head-dim values per lane in a V fragment / O
+    constexpr int HT = 16 * NT;  // head slots of the workgroup
+
+    __shared__ float sm_o[HT * D];
+    __shared__ float sm_m[HT];
+    __shared__ float sm_l[HT];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int s = blockIdx.x % S;
+    const int bg = blockIdx.x / S;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int n = seqlens[b];
+    const int start = s * chunk;
+    const int end = min(start + chunk, n);
+    if (S > 1 && start >= end) return;  // empty split: the merge skips it
+
+    const int64_t rs = (int64_t)Hkv * D;  // elements between consecutive keys
+    const uint16_t* kb = kc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const uint16_t* vb = vc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const int h0 = g * gsize;
+
+    bf16x8 qB[NT][KI];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int hq = 16 * nt + col;
+        const bool ok = hq < gsize;
+        const uint16_t* qp = q + ((int64_t)b * Hq + h0 + (ok ? hq : 0)) * D + 8 * grp;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) qB[nt][i] = as_bf16x8(load16(qp + 32 * i, ok));
+    }
+
+    f32x4 O[NT][EPL];
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+        l_run[nt] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) O[nt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    typedef typename VFragT<D>::T VT;
+    for (int key0 = start + wave * kDecodeStep; key0 < end; key0 += kDecodeWaves * kDecodeStep) {
+        u32x4 kA[2][KI];
+        VT vB[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int key = key0 + 16 * t + col;
+            const uint16_t* kp = kb + (int64_t)key * rs + 8 * grp;
+#pragma unroll
+            for (int i = 0; i < KI; ++i) kA[t][i] = load16(kp + 32 * i, key < end);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * t + 4 * grp + r;
+                vB[t][r] = load_vfrag<D>(vb + (int64_t)key * rs + EPL * col, key < end);
+            }
+
+        // V fragments for the P*V product: element 4t+r of lane (col, grp) is
+        // V[key0 + 16t + 4grp + r][EPL*col + e].
+        u32x4 vT[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = j >> 1, r = 2 * (j & 1);
+                const uint32_t w0 = vB[t][r][e >> 1];
+                const uint32_t w1 = vB[t][r + 1][e >> 1];
+                vT[e][j] = (e & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+            }
+
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float p[8];
+            float mx = kNegInf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < KI; ++i) acc = mfma16x16x32(as_bf16x8(kA[t][i]), qB[nt][i], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key0 + 16 * t + 4 * grp + r;
+                    const float sv = key < end ? acc[r] * c_log2 : kNegInf;
+                    p[4 * t + r] = sv;
+                    mx = fmaxf(mx, sv);
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[nt], mx);
+            const float alpha = fast_exp2(m_run[nt] - m_new);
+            m_run[nt] = m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                p[x] = fast_exp2(p[x] - m_new);
+                psum += p[x];
+            }
+            l_run[nt] = l_run[nt] * alpha + psum;
+
+            // Rescale O: its rows are heads 16nt + 4grp + r, whose alpha sits in lane 4grp + r.
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) O[nt][e][r] *= ar;
+            }
+
+            u32x4 phi, plo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t a = __float_as_uint(p[2 * j]);
+                const uint32_t c = __float_as_uint(p[2 * j + 1]);
+                phi[j] = pack_hi16(a, c);
+                const float al = p[2 * j] - __uint_as_float(a & 0xffff0000u);
+                const float cl = p[2 * j + 1] - __uint_as_float(c & 0xffff0000u);
+                plo[j] = pack_bf16x2_rne(al, cl);
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                O[nt][e] = mfma16x16x32(as_bf16x8(phi), as_bf16x8(vT[e]), O[nt][e]);
+                O[nt][e] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vT[e]), O[nt][e]);
+            }
+        }
+    }
+
+    // Sum of weights across the four lane groups that share a head.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        l_run[nt] += __shfl_xor(l_run[nt], 16);
+        l_run[nt] += __shfl_xor(l_run[nt], 32);
+    }
+
+    // Combine the waves of the workgroup in LDS, one wave at a time.
+    if (wave == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 16 * nt + 4 * grp + r;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_o[h * D + EPL * col + e] = O[nt][e][r];
+            }
+            if (grp == 0) {
+                sm_m[16 * nt + col] = m_run[nt];
+                sm_l[16 * nt + col] = l_run[nt];
+            }
+        }
+    }
+    for (int w = 1; w < kDecodeWaves; ++w) {
+        __syncthreads();
+        if (wave == w) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int h = 16 * nt + 4 * grp + r;
+                    const float mo = sm_m[h];
+                    const float mw = __shfl(m_run[nt], 4 * grp + r);
+                    const float M = fmaxf(mo, mw);
+                    const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
+                    const float fb = M == kNegInf ? 0.f : fast_exp2(mw - M);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const int idx = h * D + EPL * col + e;
+                        sm_o[idx] = fa * sm_o[idx] + fb * O[nt][e][r];
+                    }
+                }
+                const float mo = sm_m[16 * nt + col];
+                const float lo = sm_l[16 * nt + col];
+                const float M = fmaxf(mo, m_run[nt]);
+                const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
+                const float fb = M == kNegInf ? 0.f : fast_exp2(m_run[nt] - M);
+                if (grp == 0) {
+                    sm_m[16 * nt + col] = M;
+                    sm_l[16 * nt + col] = fa * lo + fb * l_run[nt];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    constexpr int C8 = D / 8;
+    const int items = gsize * C8;
+    for (int it = threadIdx.x; it < items; it += kDecodeThreads) {
+        const int h = it / C8;
+        const int c = (it % C8) * 8;
+        const float* src = sm_o + h * D + c;
+        const int64_t row = (int64_t)b * Hq + h0 + h;
+        if (S == 1) {
+            const float l = sm_l[h];
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x0 = l > 0.f ? src[2 * j] / l : 0.f;
+                const float x1 = l > 0.f ? src[2 * j + 1] / l : 0.f;
+                o[j] = pack_bf16x2_rne(x0, x1);
+            }
+            *reinterpret_cast<u32x4*>(out + row * D + c) = o;
+        } else {
+            float* dst = ws_acc + (row * S + s) * D + c;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4], src[5], src[6], src[7]};
+            if (c == 0) {
+                ws_ml[(row * S + s) * 2] = sm_m[h];
+                ws_ml[(row * S + s) * 2 + 1] = sm_l[h];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 split kernel on the vector ALUs (fp32 inputs).
+//
+// Per tile of 64 keys: scores for every (head of the group, key) pair into
+// LDS, per-head online-softmax update, then each thread accumulates its
+// (head, head-dim) outputs over the tile.  The query is staged in LDS
+// already multiplied by scale*log2(e).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
+    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    const int32_t* __restrict__ seqlens, int Hq, int Hkv, int Lmax, int gsize, int S, int chunk,
+    float c_log2, float* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    constexpr int TILE = 64;
+    constexpr int MAXG = 64;
+    constexpr int ACC = MAXG * D / kDecodeThreads;
+
+    __shared__ float sq[MAXG * D];
+    __shared__ float ss[MAXG * TILE];
+    __shared__ float sm[MAXG], sl[MAXG], sa[MAXG];
+
+    const int tid = threadIdx.x;
+    const int s = blockIdx.x % S;
+    const int bg = blockIdx.x / S;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int n = seqlens[b];
+    const int start = s * chunk;
+    const int end = min(start + chunk, n);
+    if (S > 1 && start >= end) return;
+    const int h0 = g * gsize;
+    const int64_t rs = (int64_t)Hkv * D;
+    const float* kb = kc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const float* vb = vc + ((int64_t)b * Lmax * Hkv + g) * D;
+
+    for (int idx = tid; idx < gsize * D; idx += kDecodeThreads)
+        sq[idx] = q[((int64_t)b * Hq + h0) * D + idx] * c_log2;
+    for (int h = tid; h < gsize; h += kDecodeThreads) {
+        sm[h] = kNegInf;
+        sl[h] = 0.f;
+    }
+    float acc[ACC];
+#pragma unroll
+    for (int i = 0; i < ACC; ++i) acc[i] = 0.f;
+    __syncthreads();
+
+    for (int t0 = start; t0 < end; t0 += TILE) {
+        const int cnt = min(TILE, end - t0);
+        for (int idx = tid; idx < gsize * TILE; idx += kDecodeThreads) {
+            const int h = idx / TILE, j = idx % TILE;
+            float sc = kNegInf;
+            if (j < cnt) {
+                const float* kr = kb + (int64_t)(t0 + j) * rs;
+                const float* qh = sq + h * D;
+                float dot = 0.f;
+                for (int c = 0; c < D; ++c) dot += qh[c] * kr[c];
+                sc = dot;
+            }
+            ss[h * TILE + j] = sc;
+        }
+        __syncthreads();
+        for (int h = tid; h < gsize; h += kDecodeThreads) {
+            float mx = kNegInf;
+            for (int j = 0; j < cnt; ++j) mx = fmaxf(mx, ss[h * TILE + j]);
+            const float mn = fmaxf(sm[h], mx);
+            const float a = fast_exp2(sm[h] - mn);
+            float sum = 0.f;
+            for (int j = 0; j < TILE; ++j) {
+                const float pj = j < cnt ? fast_exp2(ss[h * TILE + j] - mn) : 0.f;
+                ss[h * TILE + j] = pj;
+                sum += pj;
+            }
+            sl[h] = sl[h] * a + sum;
+            sm[h] = mn;
+            sa[h] = a;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < ACC; ++i) {
+            const int idx = tid + kDecodeThreads * i;
+            if (idx < gsize * D) {
+                const int h = idx / D, c = idx % D;
+                float a = acc[i] * sa[h];
+                for (int j = 0; j < cnt; ++j) a += ss[h * TILE + j] * vb[(int64_t)(t0 + j) * rs + c];
+                acc[i] = a;
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < ACC; ++i) {
+        const int idx = tid + kDecodeThreads * i;
+        if (idx < gsize * D) {
+            const int h = idx / D, c = idx % D;
+            const int64_t row = (int64_t)b * Hq + h0 + h;
+            if (S == 1) {
+                out[row * D + c] = sl[h] > 0.f ? acc[i] / sl[h] : 0.f;
+            } else {
+                ws_acc[(row * S + s) * D + c] = acc[i];
+                if (c == 0) {
+                    ws_ml[(row * S + s) * 2] = sm[h];
+                    ws_ml[(row * S + s) * 2 + 1] = sl[h];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split partials: M = max_s m_s, out = sum_s 2^(m_s-M) acc_s /
+// sum_s 2^(m_s-M) l_s over the non-empty splits s < ceil(seqlens[b]/chunk).
+// One 64-lane workgroup per (b, h) row.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16OUT>
+__global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws_acc,
+                                                   const float* __restrict__ ws_ml,
+                                                   const int32_t* __restrict__ seqlens, int Hq,
+                                                   int S, int chunk, void* __restrict__ out) {
+    constexpr int PER = D / 64;
+    const int64_t row = blockIdx.x;
+    const int b = (int)(row / Hq);
+    const int n = seqlens[b];
+    const int se = min(S, (n + chunk - 1) / chunk);
+    const int c0 = threadIdx.x * PER;
+    const float* ml = ws_ml + row * S * 2;
+    float M = kNegInf;
+    for (int s = 0; s < se; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f, acc[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+    for (int s = 0; s < se; ++s) {
+        const float f = fast_exp2(ml[2 * s] - M);
+        L += f * ml[2 * s + 1];
+        const float* a = ws_acc + (row * S + s) * D + c0;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] += f * a[p];
+    }
+    float o[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) o[p] = L > 0.f ? acc[p] / L : 0.f;
+    if (BF16OUT) {
+        uint16_t* dst = static_cast<uint16_t*>(out) + row * D + c0;
+        if (PER == 2)
+            *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2_rne(o[0], o[PER - 1]);
+        else
+            dst[0] = (uint16_t)f32_to_bf16_rne(o[0]);
+    } else {
+        float* dst = static_cast<float*>(out) + row * D + c0;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) dst[p] = o[p];
+    }
+}
+
+}  // namespace gqa

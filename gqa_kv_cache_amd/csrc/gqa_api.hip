@@ -1,0 +1,275 @@
+// libgqa: C ABI entry points (declared in include/gqa.h).
+//
+// Host side only: argument validation, split planning, workspace layout and
+// kernel launches.  Every step of the computation runs in the HIP kernels
+// included below.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "gqa.h"
+#include "common.hpp"
+#include "decode.hpp"
+#include "prefill.hpp"
+
+namespace {
+
+constexpr int kMaxGroup = 64;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, cached per device.
+gqa_status current_cu_count(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GQA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return GQA_OK;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return GQA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return GQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct DecodePlan {
+    int splits;  // pieces the cached length is cut into
+    int chunk;   // keys per piece
+};
+
+gqa_status check_heads(int Hq, int Hkv, int d) {
+    if (Hq <= 0 || Hkv <= 0) return GQA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return GQA_ERR_GROUP;
+    if (d != 64 && d != 128) return GQA_ERR_HEADDIM;
+    if (Hq / Hkv > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+gqa_status plan_decode(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype, int num_splits,
+                       DecodePlan* plan) {
+    if (B <= 0 || Lmax <= 0) return GQA_ERR_SHAPE;
+    gqa_status st = check_heads(Hq, Hkv, d);
+    if (st != GQA_OK) return st;
+    if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
+    if (num_splits < 0 || num_splits > Lmax) return GQA_ERR_UNSUPPORTED;
+    int64_t chunk;
+    if (num_splits == 0) {
+        // Aim for about four workgroups per compute unit over the whole
+        // (sequence, KV head, piece) grid, with pieces of 128..2048 keys.
+        int cus = 0;
+        st = current_cu_count(&cus);
+        if (st != GQA_OK) return st;
+        const int64_t target = 4LL * cus;
+        const int64_t pairs = (int64_t)B * Hkv;
+        chunk = cdiv(cdiv((int64_t)Lmax * pairs, target), 128) * 128;
+        if (chunk < 128) chunk = 128;
+        if (chunk > 2048) chunk = 2048;
+        if (chunk > Lmax) chunk = Lmax;
+    } else {
+        chunk = cdiv(Lmax, num_splits);
+    }
+    const int64_t splits = cdiv(Lmax, chunk);
+    if ((int64_t)B * Hkv * splits > INT_MAX) return GQA_ERR_SHAPE;
+    plan->splits = (int)splits;
+    plan->chunk = (int)chunk;
+    return GQA_OK;
+}
+
+// Workspace: acc [B, Hq, splits, d] fp32, then (m, l) [B, Hq, splits, 2] fp32.
+size_t workspace_acc_bytes(int B, int Hq, int d, int splits) {
+    return (size_t)B * Hq * splits * d * sizeof(float);
+}
+size_t workspace_bytes_for(int B, int Hq, int d, int splits) {
+    if (splits <= 1) return 0;
+    return workspace_acc_bytes(B, Hq, d, splits) + (size_t)B * Hq * splits * 2 * sizeof(float);
+}
+
+template <int D>
+void launch_split_bf16(int nt, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const int32_t* sl, int Hq, int Hkv, int Lmax, int gs, int S,
+                       int chunk, float c, uint16_t* out, float* wa, float* wm) {
+    dim3 block(gqa::kDecodeThreads);
+    switch (nt) {
+        case 1: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 1>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
+        case 2: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 2>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
+        case 3: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 3>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
+        default: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 4>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_str(gqa_status s) {
+    switch (s) {
+        case GQA_OK: return "GQA_OK";
+        case GQA_ERR_NULL: return "GQA_ERR_NULL: a required pointer is NULL";
+        case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE: a size is out of range";
+        case GQA_ERR_GROUP: return "GQA_ERR_GROUP: Hq is not a multiple of Hkv";
+        case GQA_ERR_HEADDIM: return "GQA_ERR_HEADDIM: head dim must be 64 or 128";
+        case GQA_ERR_DTYPE: return "GQA_ERR_DTYPE: dtype not supported by this call";
+        case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: a data pointer is not 16-byte aligned";
+        case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+        case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: group size above 64 or num_splits out of range";
+        case GQA_ERR_HIP: return "GQA_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "GQA status: unknown code";
+}
+
+gqa_status gqa_decode_num_splits(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
+                                 int num_splits, int* splits) {
+    if (!splits) return GQA_ERR_NULL;
+    DecodePlan plan;
+    gqa_status st = plan_decode(B, Hq, Hkv, d, Lmax, dtype, num_splits, &plan);
+    if (st != GQA_OK) return st;
+    *splits = plan.splits;
+    return GQA_OK;
+}
+
+gqa_status gqa_decode_workspace_size(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
+                                     int num_splits, size_t* bytes) {
+    if (!bytes) return GQA_ERR_NULL;
+    DecodePlan plan;
+    gqa_status st = plan_decode(B, Hq, Hkv, d, Lmax, dtype, num_splits, &plan);
+    if (st != GQA_OK) return st;
+    *bytes = workspace_bytes_for(B, Hq, d, plan.splits);
+    return GQA_OK;
+}
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax, float scale,
+                      gqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                      int num_splits, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !out) return GQA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return GQA_ERR_ALIGN;
+    // Validate sizes before touching the runtime.
+    if (B <= 0 || Lmax <= 0) return GQA_ERR_SHAPE;
+    gqa_status st = check_heads(Hq, Hkv, d);
+    if (st != GQA_OK) return st;
+    if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
+    if (num_splits < 0 || num_splits > Lmax) return GQA_ERR_UNSUPPORTED;
+    DecodePlan plan;  // queries the device only when num_splits == 0
+    st = plan_decode(B, Hq, Hkv, d, Lmax, dtype, num_splits, &plan);
+    if (st != GQA_OK) return st;
+    const size_t need = workspace_bytes_for(B, Hq, d, plan.splits);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return GQA_ERR_WORKSPACE;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int gs = Hq / Hkv;
+    const int S = plan.splits;
+    const float c = scale * gqa::kLog2e;
+    float* ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+    float* ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                   workspace_acc_bytes(B, Hq, d, S))
+                        : nullptr;
+    dim3 grid((unsigned)((int64_t)B * Hkv * S));
+
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    if (dtype == GQA_BF16) {
+        const int nt = (gs + 15) / 16;
+        auto qp = static_cast<const uint16_t*>(q);
+        auto kp = static_cast<const uint16_t*>(k_cache);
+        auto vp = static_cast<const uint16_t*>(v_cache);
+        auto op = static_cast<uint16_t*>(out);
+        if (d == 128)
+            launch_split_bf16<128>(nt, grid, hs, qp, kp, vp, seqlens, Hq, Hkv, Lmax, gs, S, plan.chunk, c, op, ws_acc, ws_ml);
+        else
+            launch_split_bf16<64>(nt, grid, hs, qp, kp, vp, seqlens, Hq, Hkv, Lmax, gs, S, plan.chunk, c, op, ws_acc, ws_ml);
+    } else {
+        auto qp = static_cast<const float*>(q);
+        auto kp = static_cast<const float*>(k_cache);
+        auto vp = static_cast<const float*>(v_cache);
+        auto op = static_cast<float*>(out);
+        dim3 block(gqa::kDecodeThreads);
+        if (d == 128)
+            hipLaunchKernelGGL((gqa::decode_split_f32<128>), grid, block, 0, hs, qp, kp, vp, seqlens, Hq, Hkv, Lmax, gs, S, plan.chunk, c, op, ws_acc, ws_ml);
+        else
+            hipLaunchKernelGGL((gqa::decode_split_f32<64>), grid, block, 0, hs, qp, kp, vp, seqlens, Hq, Hkv, Lmax, gs, S, plan.chunk, c, op, ws_acc, ws_ml);
+    }
+    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    if (S > 1) {
+        dim3 mgrid((unsigned)((int64_t)B * Hq));
+        dim3 mblock(64);
+        if (dtype == GQA_BF16) {
+            if (d == 128)
+                hipLaunchKernelGGL((gqa::decode_merge<128, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+            else
+                hipLaunchKernelGGL((gqa::decode_merge<64, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+        } else {
+            if (d == 128)
+                hipLaunchKernelGGL((gqa::decode_merge<128, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+            else
+                hipLaunchKernelGGL((gqa::decode_merge<64, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+        }
+        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    }
+    return GQA_OK;
+}
+
+gqa_status gqa_prefill(const void* q, const void* k, const void* v, int B, int P, int Hq, int Hkv,
+                       int d, int causal, float scale, gqa_dtype dtype, void* out, void* stream) {
+    if (!q || !k || !v || !out) return GQA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
+    if (B <= 0 || P <= 0) return GQA_ERR_SHAPE;
+    gqa_status st = check_heads(Hq, Hkv, d);
+    if (st != GQA_OK) return st;
+    if (dtype != GQA_BF16) return GQA_ERR_DTYPE;
+    if ((int64_t)B * Hq * cdiv(P, gqa::kPrefillRows) > INT_MAX) return GQA_ERR_SHAPE;
+    (void)hipGetLastError();
+    if (!gqa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                             static_cast<const uint16_t*>(v), B, P, Hq, Hkv, d, causal != 0,
+                             scale * gqa::kLog2e, static_cast<uint16_t*>(out),
+                             static_cast<hipStream_t>(stream)))
+        return GQA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+}
+
+uint64_t gqa_kv_cache_elems(uint64_t L, uint64_t Hkv, uint64_t d) { return 2ull * L * Hkv * d; }
+
+uint64_t gqa_decode_bytes(const int32_t* host_seqlens, int B, int Hq, int Hkv, int d,
+                          gqa_dtype dtype) {
+    const uint64_t elt = dtype == GQA_BF16 ? 2 : dtype == GQA_F32 ? 4 : 0;
+    if (!elt || !host_seqlens || B <= 0) return 0;
+    uint64_t rows = 0;
+    for (int b = 0; b < B; ++b) rows += host_seqlens[b] > 0 ? (uint64_t)host_seqlens[b] : 0;
+    const uint64_t kv = rows * gqa_kv_cache_elems(1, (uint64_t)Hkv, (uint64_t)d) * elt;
+    const uint64_t q_and_out = 2ull * (uint64_t)B * Hq * d * elt;
+    return kv + q_and_out;
+}
+
+uint64_t gqa_decode_flops(const int32_t* host_seqlens, int B, int Hq, int d) {
+    if (!host_seqlens || B <= 0) return 0;
+    uint64_t rows = 0;
+    for (int b = 0; b < B; ++b) rows += host_seqlens[b] > 0 ? (uint64_t)host_seqlens[b] : 0;
+    return 4ull * (uint64_t)Hq * (uint64_t)d * rows;
+}
+
+uint64_t gqa_prefill_flops(int B, int P, int Hq, int d, int causal) {
+    if (B <= 0 || P <= 0) return 0;
+    const uint64_t p = (uint64_t)P;
+    const uint64_t pairs = causal ? p * (p + 1) / 2 : p * p;
+    return 4ull * (uint64_t)B * Hq * d * pairs;
+}
+
+uint64_t gqa_prefill_bytes(int B, int P, int Hq, int Hkv, int d, gqa_dtype dtype) {
+    const uint64_t elt = dtype == GQA_BF16 ? 2 : dtype == GQA_F32 ? 4 : 0;
+    if (B <= 0 || P <= 0) return 0;
+    return (uint64_t)B * P * d * elt * (2ull * Hq + 2ull * Hkv);
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+/*
+ * gqa.h -- C ABI of libgqa: grouped-query attention (GQA) over a KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method.  Hq query heads share Hkv key/value heads in contiguous groups of
+ * Gs = Hq / Hkv: query head h (0-indexed) reads KV head g = floor(h / Gs),
+ * the 0-indexed form of g(h) = ceil(h / (H/G)) in "GQA reading notes"
+ * (zhongzhuzhou.org), section "方法详解 > GQA 架构", where
+ * head_h = softmax(q_h K_g^T * scale) V_g.  Hkv = Hq is multi-head attention
+ * and Hkv = 1 multi-query attention ("从MHA到GQA", gzher.com, GQA section).
+ * Hq must be a multiple of Hkv ("查询头保持不变，只减少键值头", ttlab lesson,
+ * section on the three names on one axis).
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense, row-major, contiguous device buffers; element
+ *     type is given by gqa_dtype.  bf16 is the 16-bit brain float, stored as
+ *     its bit pattern.  q, caches and out share one dtype.
+ *   - Every data pointer must be 16-byte aligned (GQA_ERR_ALIGN otherwise).
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after return and has no state beyond a per-device
+ *     cache of the compute-unit count.
+ *   - Calls validate their arguments on the host first; a validation error
+ *     returns before any device work, and nothing is written.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronises.  A launch failure returns
+ *     GQA_ERR_HIP; device faults surface at the caller's next synchronisation.
+ *   - Arithmetic is fp32 throughout (bf16 inputs are widened exactly; bf16
+ *     products are formed exactly in fp32 by the matrix cores); bf16 outputs
+ *     are rounded to nearest-even.  Results are deterministic run to run.
+ *   - Calls are reentrant and thread-safe.  `out` must not alias an input.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_NULL = 1,        /* a required pointer is NULL */
+    GQA_ERR_SHAPE = 2,       /* B, Hq, Hkv, Lmax or P out of range (see each call) */
+    GQA_ERR_GROUP = 3,       /* Hq is not a multiple of Hkv */
+    GQA_ERR_HEADDIM = 4,     /* d is not 64 or 128 */
+    GQA_ERR_DTYPE = 5,       /* dtype not supported by this call */
+    GQA_ERR_ALIGN = 6,       /* a data pointer is not 16-byte aligned */
+    GQA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+    GQA_ERR_UNSUPPORTED = 8, /* group size Hq/Hkv above 64, or num_splits out of range */
+    GQA_ERR_HIP = 9          /* the HIP runtime reported an error */
+} gqa_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *gqa_status_str(gqa_status s);
+
+/* ------------------------------------------------------------------------
+ * Decode: one new query token per sequence against its cached K/V rows.
+ *
+ * Follows Algorithm 2 (GQA decode, step t) of "GQA reading notes", the
+ * per-query-head part: for every sequence b and query head h,
+ *   s_j = scale * <q[b,h,:], k_cache[b,j,g,:]>  for j < seqlens[b],
+ *   out[b,h,:] = sum_j softmax(s)_j * v_cache[b,j,g,:],   g = h / (Hq/Hkv).
+ * The new token's K/V must already be written at row seqlens[b]-1 (the
+ * append of that algorithm happens before this call).  Each K/V row of a
+ * group is read from memory once and serves all Hq/Hkv query heads of the
+ * group (same page, walkthrough of Algorithm 2).
+ *
+ *   q        [B, Hq, d]
+ *   k_cache  [B, Lmax, Hkv, d]   rows j >= seqlens[b] are never read
+ *   v_cache  [B, Lmax, Hkv, d]
+ *   seqlens  [B] int32, DEVICE memory; precondition 0 <= seqlens[b] <= Lmax
+ *            (not checked: it lives on the device).  seqlens[b] == 0 gives
+ *            out[b,:,:] = 0.
+ *   out      [B, Hq, d]
+ *   scale    softmax scale, normally 1/sqrt(d)
+ *   dtype    GQA_F32 or GQA_BF16
+ *   d        64 or 128;  1 <= Hq/Hkv <= 64;  B, Hq, Hkv, Lmax >= 1
+ *   num_splits  0 = choose automatically; otherwise the number of pieces
+ *            the cached length is cut into (1 <= num_splits <= Lmax).  With
+ *            more than one piece, partial results (running max, sum of
+ *            weights, weighted sum) go to `workspace` and a second kernel
+ *            merges them.
+ *   workspace, workspace_bytes  caller-provided device scratch of at least
+ *            gqa_decode_workspace_size() bytes; may be NULL when that size is 0.
+ *
+ * Returns GQA_OK or an error code; see the conventions above.
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seqlens, int B, int Hq, int Hkv, int d, int Lmax,
+                      float scale, gqa_dtype dtype, void *out, void *workspace,
+                      size_t workspace_bytes, int num_splits, void *stream);
+
+/* Number of pieces gqa_decode will cut the cached length into for these
+ * arguments (num_splits = 0 asks for the automatic choice, which depends on
+ * the current device's compute-unit count).  Writes it to *splits. */
+gqa_status gqa_decode_num_splits(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
+                                 int num_splits, int *splits);
+
+/* Workspace bytes gqa_decode needs for these arguments (0 when it needs
+ * none).  Same argument meaning as gqa_decode.  Writes it to *bytes. */
+gqa_status gqa_decode_workspace_size(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
+                                     int num_splits, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * Prefill: the whole prompt attends to itself in parallel.
+ *
+ * With causal != 0, prompt position i of sequence b attends to positions
+ * 0..i only (the causal mask of the prefill phase, "从MHA到GQA", section on
+ * why the question becomes how KV is stored); with causal == 0 to all P.
+ *   out[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], k[b,j,g,:]>) v[b,j,g,:]
+ *
+ *   q    [B, P, Hq, d]
+ *   k    [B, P, Hkv, d]
+ *   v    [B, P, Hkv, d]
+ *   out  [B, P, Hq, d]
+ *   dtype  GQA_BF16 only (the matrix-core path); GQA_F32 -> GQA_ERR_DTYPE
+ *   d      64 or 128;  1 <= Hq/Hkv <= 64;  B, P, Hq, Hkv >= 1
+ *
+ * Returns GQA_OK or an error code; see the conventions above.
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P, int Hq,
+                       int Hkv, int d, int causal, float scale, gqa_dtype dtype, void *out,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * Counts (host only, exact integers).
+ *
+ * KV-cache elements per layer and sequence = 2 * L * Hkv * d: the leading 2
+ * is K and V ("查询头保持不变，只减少键值头", section "什么减少，什么不减少";
+ * "GQA reading notes", section 3, equation S_KV).
+ * ------------------------------------------------------------------------ */
+uint64_t gqa_kv_cache_elems(uint64_t L, uint64_t Hkv, uint64_t d);
+
+/* Algorithmic bytes of one gqa_decode call: every valid K and V row read
+ * once per KV head, plus q read and out written once.  host_seqlens is a
+ * HOST array of B lengths.  Returns 0 for an unknown dtype. */
+uint64_t gqa_decode_bytes(const int32_t *host_seqlens, int B, int Hq, int Hkv, int d,
+                          gqa_dtype dtype);
+
+/* FLOP of one gqa_decode call: 2 per multiply-add, scores plus weighted sum:
+ * 4 * Hq * d * sum(seqlens).  It holds no Hkv term (ttlab lesson, same
+ * section: the attention multiplications have no group count). */
+uint64_t gqa_decode_flops(const int32_t *host_seqlens, int B, int Hq, int d);
+
+/* FLOP of one gqa_prefill call: 4 * B * Hq * d * pairs, where pairs =
+ * P(P+1)/2 unmasked query-key pairs if causal, P*P otherwise. */
+uint64_t gqa_prefill_flops(int B, int P, int Hq, int d, int causal);
+
+/* Algorithmic bytes of one gqa_prefill call: q, k, v read once, out written once. */
+uint64_t gqa_prefill_bytes(int B, int P, int Hq, int Hkv, int d, gqa_dtype dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI: exports, header, argument validation, counts.
+
+No test here launches GPU work: every call either is a pure host function
+(counts, planning with an explicit split count) or fails validation before
+the library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gqa_inputs as gi
+import gqa_kv_cache_amd as gqa
+from gqa_kv_cache_amd._native import Status
+from oracle import counts as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+FAKE = 0x10000  # aligned, non-null; never dereferenced by the validation paths used here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gqa.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    assert set(names) == set(gqa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gqa.LIBRARY_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(r"\bT %s$" % n, out, flags=re.M), n
+
+
+def test_header_is_plain_c99(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "gqa.h"\nint main(void){ return (int)GQA_OK; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                    "-I", os.path.dirname(HEADER), str(src)], check=True)
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, d=128, Lmax=64, scale=0.1,
+             dt=gqa.BF16, out=FAKE, ws=None, wsb=0, ns=1, stream=None)
+    a.update(kw)
+    return gqa.load().gqa_decode(a["q"], a["k"], a["v"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                 a["Lmax"], a["scale"], a["dt"], a["out"], a["ws"], a["wsb"],
+                                 a["ns"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), Status.ERR_NULL),
+    (dict(sl=None), Status.ERR_NULL),
+    (dict(out=None), Status.ERR_NULL),
+    (dict(k=FAKE + 2), Status.ERR_ALIGN),
+    (dict(out=FAKE + 8), Status.ERR_ALIGN),
+    (dict(B=0), Status.ERR_SHAPE),
+    (dict(Lmax=0), Status.ERR_SHAPE),
+    (dict(Hkv=0), Status.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), Status.ERR_GROUP),
+    (dict(d=96), Status.ERR_HEADDIM),
+    (dict(d=256), Status.ERR_HEADDIM),
+    (dict(dt=7), Status.ERR_DTYPE),
+    (dict(Hq=128, Hkv=1), Status.ERR_UNSUPPORTED),
+    (dict(ns=-1), Status.ERR_UNSUPPORTED),
+    (dict(ns=65), Status.ERR_UNSUPPORTED),
+    (dict(ns=4, ws=None), Status.ERR_WORKSPACE),
+    (dict(ns=4, ws=FAKE, wsb=16), Status.ERR_WORKSPACE),
+    (dict(ns=4, ws=FAKE + 4, wsb=1 << 30), Status.ERR_WORKSPACE),
+])
+def test_decode_validation(kw, expect):
+    assert _decode(**kw) == expect
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, P=16, Hq=8, Hkv=2, d=128, causal=1, scale=0.1,
+             dt=gqa.BF16, out=FAKE, stream=None)
+    a.update(kw)
+    return gqa.load().gqa_prefill(a["q"], a["k"], a["v"], a["B"], a["P"], a["Hq"], a["Hkv"], a["d"],
+                                  a["causal"], a["scale"], a["dt"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(v=None), Status.ERR_NULL),
+    (dict(q=FAKE + 2), Status.ERR_ALIGN),
+    (dict(P=0), Status.ERR_SHAPE),
+    (dict(Hq=8, Hkv=3), Status.ERR_GROUP),
+    (dict(d=32), Status.ERR_HEADDIM),
+    (dict(dt=gqa.F32), Status.ERR_DTYPE),
+    (dict(Hq=65 * 2, Hkv=2), Status.ERR_UNSUPPORTED),
+])
+def test_prefill_validation(kw, expect):
+    assert _prefill(**kw) == expect
+
+
+def test_status_strings():
+    for s in Status:
+        assert gqa.status_str(int(s)).startswith("GQA_")
+    assert "unknown" in gqa.status_str(99)
+
+
+@pytest.mark.parametrize("Lmax,ns,expect", [(4096, 4, 4), (4096, 1, 1), (10, 4, 4), (10, 6, 5),
+                                            (10, 10, 10), (1, 1, 1), (32768, 16, 16)])
+def test_forced_split_plan(Lmax, ns, expect):
+    assert gqa.decode_num_splits(4, 8, 2, 128, Lmax, gqa.BF16, ns) == expect
+    ws = gqa.decode_workspace_size(4, 8, 2, 128, Lmax, gqa.BF16, ns)
+    assert ws == (0 if expect == 1 else 4 * 8 * expect * (128 + 2) * 4)
+
+
+# --- library counts against the oracle's independently written counts -----
+
+def _workloads():
+    yield "tiny", [128], 8, 2, 64, 4
+    yield "70b", [4096] * 32, 64, 8, 128, 2
+    for h in gi.SWEEP_HKV:
+        yield "sweep%d" % h, [2048] * 16, 64, h, 128, 2
+    yield "ragged", list(gi.ragged_seqlens()), 32, 8, 128, 2
+
+
+@pytest.mark.parametrize("name,seq,Hq,Hkv,d,elt", list(_workloads()), ids=lambda x: str(x)[:12])
+def test_decode_counts_match_oracle(name, seq, Hq, Hkv, d, elt):
+    dt = gqa.BF16 if elt == 2 else gqa.F32
+    assert gqa.decode_bytes(seq, Hq, Hkv, d, dt) == oc.decode_bytes(seq, Hq, Hkv, d, elt)
+    assert gqa.decode_flops(seq, Hq, d) == oc.decode_flops(seq, Hq, d)
+
+
+def test_decode_bytes_headline_value():
+    # K+V = 2*32*4096*8*128*2 bytes, plus q and out once each
+    assert gqa.decode_bytes([4096] * 32, 64, 8, 128, gqa.BF16) == 537919488
+
+
+@pytest.mark.parametrize("L,Hkv,d", [(1, 1, 1), (4096, 8, 128), (32768, 8, 128), (131072, 32, 128)])
+def test_kv_elems_match_oracle(L, Hkv, d):
+    assert gqa.kv_cache_elems(L, Hkv, d) == oc.kv_cache_elems(L, Hkv, d)
+
+
+@pytest.mark.parametrize("B,P,Hq,Hkv,d", [(2, 4096, 32, 8, 128), (1, 1, 4, 4, 64), (3, 77, 8, 2, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_counts_match_oracle(B, P, Hq, Hkv, d, causal):
+    assert gqa.prefill_flops(B, P, Hq, d, causal) == oc.prefill_flops(B, P, Hq, d, causal)
+    assert gqa.prefill_bytes(B, P, Hq, Hkv, d, gqa.BF16) == oc.prefill_bytes(B, P, Hq, Hkv, d, 2)
+
+
+def test_prefill_flops_headline_value():
+    assert gqa.prefill_flops(2, 4096, 32, 128, True) == 274945015808

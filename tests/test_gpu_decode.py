@@ -1,0 +1,181 @@
+"""GPU parity of gqa_decode against the fp64 CPU oracle (needs an MI355X).
+
+Tolerances: fp32 inputs max |gpu - oracle| <= 1e-5; bf16 inputs (fp32
+accumulation) |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise.  Cache rows
+at or beyond seqlens[b] hold NaN, so any read of them would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import gqa_kv_cache_amd as gqa
+from oracle import reference as orc
+from tests.gpu_util import bits, from_dev, to_dev
+from tests.helpers import bf16_tol_ok, f32_tol_ok, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(case, num_splits=0, out=None, workspace=None):
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    sl = torch.from_numpy(case.seqlens).cuda()
+    o = gqa.decode(q, k, v, sl, case.scale, out=out, num_splits=num_splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return o
+
+
+def check(case, got, ref):
+    if case.dtype == "f32":
+        ok, err = f32_tol_ok(got, ref)
+    else:
+        ok, err = bf16_tol_ok(got, ref)
+    assert ok, "%s: max abs err %.3g" % (case.name, err)
+    assert np.all(np.isfinite(got))
+    return err
+
+
+# --- the tiny fp32 workload: GQA, MHA and MQA on the same q ---------------
+
+@pytest.mark.parametrize("hkv", [2, 8, 1])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 5])
+def test_tiny_fp32(hkv, splits):
+    c = gi.tiny_decode(hkv)
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale)
+    got = from_dev(run_decode(c, splits))
+    check(c, got, ref)
+
+
+# --- the 70B-class layer: full output against the oracle ------------------
+
+def test_decode_70b_full():
+    c = gi.decode_70b()
+    got = from_dev(run_decode(c))
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale)
+    err = check(c, got, ref)
+    print("decode 70b max abs err %.3g" % err)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 8])
+def test_decode_70b_forced_splits_sampled(splits):
+    c = gi.decode_70b()
+    got = from_dev(run_decode(c, splits)).reshape(-1, 128)
+    rows = np.random.default_rng(splits).choice(32 * 64, 128, replace=False)
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale, rows=rows)
+    check(c, got[rows], ref)
+
+
+# --- head-sharing sweep ----------------------------------------------------
+
+@pytest.mark.parametrize("hkv", gi.SWEEP_HKV)
+def test_sweep_full(hkv):
+    c = gi.sweep_decode(hkv)
+    got = from_dev(run_decode(c))
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale)
+    check(c, got, ref)
+
+
+# --- ragged batch at full size, NaN beyond every length, sampled rows -------
+
+def test_ragged_sampled():
+    c = gi.ragged_decode(invalid="nan")
+    got = from_dev(run_decode(c)).reshape(-1, 128)
+    assert np.all(np.isfinite(got))
+    B, Hq = 64, 32
+    rng = np.random.default_rng(44)
+    b_short, b_long = int(np.argmin(c.seqlens)), int(np.argmax(c.seqlens))
+    rows = set(rng.choice(B * Hq, 384, replace=False).tolist())
+    rows |= {b_short * Hq + h for h in range(Hq)} | {b_long * Hq + h for h in range(Hq)}
+    rows = np.array(sorted(rows))
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale, rows=rows)
+    check(c, got[rows], ref)
+
+
+# --- randomised shapes: head dims, group sizes, lengths, ragged, splits ------
+
+SEQ = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
+
+
+def _sweep_cases():
+    for d in (64, 128):
+        for G in (1, 2, 4, 8, 16, 64):
+            Hkv = 2 if G <= 16 else 1
+            for splits in (1, 3, 0):
+                yield ("bf16", d, G * Hkv, Hkv, splits)
+    for d in (64, 128):
+        for G in (1, 4, 16, 64):
+            for splits in (1, 4):
+                yield ("f32", d, G, 1, splits)
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,splits", list(_sweep_cases()))
+def test_shapes_ragged_nan_poisoned(dtype, d, Hq, Hkv, splits):
+    c = gi.decode_case(len(SEQ), Hq, Hkv, d, 300, SEQ, dtype, q_seed=d + Hq, kv_seed=Hkv + splits,
+                       invalid="nan", name="sweep_%s_d%d_Hq%d_Hkv%d_s%d" % (dtype, d, Hq, Hkv, splits))
+    got = from_dev(run_decode(c, splits))
+    ref = orc.decode(c.q, c.k, c.v, c.seqlens, c.scale)
+    check(c, got, ref)
+    assert np.all(got[0] == 0.0)  # zero-length sequence
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_long_two_sequences(splits):
+    c = gi.decode_case(2, 16, 2, 128, 4096, [4096, 4000], "bf16", q_seed=5, kv_seed=6, invalid="nan")
+    check(c, from_dev(run_decode(c, splits)), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
+
+
+def test_one_key_per_split():
+    c = gi.decode_case(3, 8, 2, 128, 100, [100, 57, 1], "bf16", q_seed=7, kv_seed=8, invalid="nan")
+    check(c, from_dev(run_decode(c, 100)), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_key_returns_v_exactly(dtype):
+    c = gi.decode_case(4, 16, 4, 128, 8, [1, 1, 1, 1], dtype, q_seed=9, kv_seed=10, invalid="nan")
+    got = from_dev(run_decode(c, 1))
+    for b in range(4):
+        for h in range(16):
+            assert np.array_equal(got[b, h], widen(c.v[b, 0, h // 4]))
+
+
+def test_gqa_equals_repeat_expanded_mha_on_gpu():
+    c = gi.decode_case(3, 32, 4, 128, 500, [500, 321, 77], "bf16", q_seed=11, kv_seed=12, invalid="nan")
+    gs = 8
+    m = gi.DecodeCase("mha", c.q, np.ascontiguousarray(np.repeat(c.k, gs, axis=2)),
+                      np.ascontiguousarray(np.repeat(c.v, gs, axis=2)), c.seqlens, c.scale, "bf16")
+    a = from_dev(run_decode(c))
+    b = from_dev(run_decode(m))
+    ok, err = bf16_tol_ok(a, b)
+    assert ok, err
+
+
+# --- memory safety and determinism ------------------------------------------
+
+def test_guard_bands_untouched():
+    c = gi.decode_case(4, 32, 8, 128, 1000, [1000, 999, 3, 640], "bf16", q_seed=13, kv_seed=14,
+                       invalid="nan")
+    splits = 4
+    n_out = 4 * 32 * 128
+    guard = 4096
+    canary = 0x5A5A
+    out_big = torch.full((n_out + 2 * guard,), canary, dtype=torch.int16, device="cuda")
+    out = out_big[guard:guard + n_out].view(torch.bfloat16).view(4, 32, 128)
+    need = gqa.decode_workspace_size(4, 32, 8, 128, 1000, gqa.BF16, splits)
+    assert need > 0
+    ws_big = torch.full((need + 2 * guard,), 0x77, dtype=torch.uint8, device="cuda")
+    ws = ws_big[guard:guard + need]
+    run_decode(c, splits, out=out, workspace=ws)
+    ob = out_big.cpu().numpy()
+    assert np.all(ob[:guard] == canary) and np.all(ob[guard + n_out:] == canary)
+    wb = ws_big.cpu().numpy()
+    assert np.all(wb[:guard] == 0x77) and np.all(wb[guard + need:] == 0x77)
+    check(c, from_dev(out), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_run_twice_bitwise(splits):
+    c = gi.decode_case(8, 64, 8, 128, 2048, [2048, 1, 700, 2047, 33, 1024, 5, 1500], "bf16",
+                       q_seed=15, kv_seed=16, invalid="nan")
+    a = bits(run_decode(c, splits))
+    b = bits(run_decode(c, splits))
+    assert np.array_equal(a, b)

@@ -1,0 +1,81 @@
+"""GPU parity of gqa_prefill against the fp64 CPU oracle (needs an MI355X).
+
+bf16 inputs with fp32 accumulation: |gpu - oracle| <= 2e-2 + 1e-2 |oracle|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import gqa_kv_cache_amd as gqa
+from oracle import reference as orc
+from tests.gpu_util import bits, from_dev, to_dev
+from tests.helpers import bf16_tol_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(c):
+    o = gqa.prefill(to_dev(c.q), to_dev(c.k), to_dev(c.v), causal=c.causal, scale=c.scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def check(name, got, ref):
+    ok, err = bf16_tol_ok(got, ref)
+    assert ok, "%s: max abs err %.3g" % (name, err)
+    assert np.all(np.isfinite(got))
+
+
+def _cases():
+    for causal in (True, False):
+        for (B, P, Hq, Hkv, d) in [(1, 1, 4, 1, 128), (2, 7, 8, 2, 128), (1, 64, 4, 4, 128),
+                                   (1, 65, 8, 1, 128), (2, 200, 6, 3, 64), (1, 129, 16, 2, 64),
+                                   (1, 300, 2, 2, 128), (1, 97, 64, 1, 128)]:
+            yield causal, B, P, Hq, Hkv, d
+
+
+@pytest.mark.parametrize("causal,B,P,Hq,Hkv,d", list(_cases()))
+def test_small_full(causal, B, P, Hq, Hkv, d):
+    c = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=P + Hq + d, causal=causal)
+    check("prefill", from_dev(run_prefill(c)), orc.prefill(c.q, c.k, c.v, causal, c.scale))
+
+
+def test_medium_full():
+    c = gi.prefill_case(1, 1024, 16, 4, 128, "bf16", seed=77)
+    check("prefill_1024", from_dev(run_prefill(c)), orc.prefill(c.q, c.k, c.v, True, c.scale))
+
+
+def test_causal_prefill_full_size_sampled():
+    c = gi.prefill_causal()
+    got = from_dev(run_prefill(c)).reshape(-1, 128)
+    B, P, Hq = 2, 4096, 32
+    rng = np.random.default_rng(55)
+    pos = np.unique(np.concatenate([rng.integers(0, P, 96), [0, 1, 31, 32, 63, 64, 127, 128, 4095]]))
+    rows = []
+    for i in pos:
+        b = int(rng.integers(0, B))
+        for h in rng.choice(Hq, 4, replace=False):
+            rows.append((b * P + int(i)) * Hq + int(h))
+    rows = np.array(sorted(set(rows)))
+    ref = orc.prefill(c.q, c.k, c.v, True, c.scale, rows=rows)
+    check(c.name, got[rows], ref)
+
+
+def test_prefill_rows_match_decode_on_gpu():
+    """Causal prefill row i equals decode over i+1 cached rows (both on the GPU)."""
+    B, P, Hq, Hkv, d = 2, 160, 8, 2, 128
+    c = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=88)
+    pre = from_dev(run_prefill(c))
+    k, v = to_dev(c.k), to_dev(c.v)
+    for i in (0, 1, 31, 32, 100, 159):
+        q = to_dev(np.ascontiguousarray(c.q[:, i]))
+        sl = torch.full((B,), i + 1, dtype=torch.int32, device="cuda")
+        dec = from_dev(gqa.decode(q, k, v, sl, c.scale))
+        ok, err = bf16_tol_ok(pre[:, i], dec)
+        assert ok, (i, err)
+
+
+def test_prefill_run_twice_bitwise():
+    c = gi.prefill_case(1, 333, 16, 4, 128, "bf16", seed=99)
+    assert np.array_equal(bits(run_prefill(c)), bits(run_prefill(c)))
