@@ -23,22 +23,163 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kDecodeStep = 32;  // keys one wave consumes per step (bf16 kernel)
 
+// Raw buffer resources: a load at a byte offset at or beyond the resource's
+// size returns zero without touching memory, so rows past seqlens[b] are
+// never read and need no branch.
+constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit raw data format (gfx9 family)
+constexpr int kStreamLoad = 2;               // cache policy "nt": data used once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kRawBufferWord3);
+}
+
+template <int D> struct DecodeShape {
+    static constexpr int KI = D / 32;     // 32-wide head-dim slices of the score MFMA
+    static constexpr int EPL = D / 16;    // head-dim values per lane in a V fragment and in O
+    static constexpr int CPR = D / 8;     // 16-byte chunks per cached row
+    static constexpr int RPI = 64 / CPR;  // rows covered by one row-pattern K load
+    static constexpr int KLD = 32 / RPI;  // K loads per 32-key step
+};
+
 template <int D> struct VFragT;
 template <> struct VFragT<128> { typedef u32x4 T; };
 template <> struct VFragT<64> { typedef u32x2 T; };
 
 template <int D>
-__device__ __forceinline__ typename VFragT<D>::T load_vfrag(const uint16_t* p, bool ok) {
-    typedef typename VFragT<D>::T T;
-    T z{};
-    if (ok) z = *reinterpret_cast<const T*>(p);
-    return z;
+__device__ __forceinline__ typename VFragT<D>::T load_vfrag(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <>
+__device__ __forceinline__ u32x4 load_vfrag<128>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamLoad);
+}
+template <>
+__device__ __forceinline__ u32x2 load_vfrag<64>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamLoad);
+}
+
+// One 32-key step of one wave, as loaded: K rows (row pattern: each load
+// covers RPI whole rows) and V rows (each load covers 4 whole rows).
+template <int D> struct DecodeStepData {
+    u32x4 kR[DecodeShape<D>::KLD];
+    typename VFragT<D>::T vB[2][4];
+};
+
+template <int D>
+__device__ __forceinline__ void decode_load_step(DecodeStepData<D>& st, __amdgpu_buffer_rsrc_t kr,
+                                                 __amdgpu_buffer_rsrc_t vr, int rs2, int key0,
+                                                 int lane) {
+    typedef DecodeShape<D> Sh;
+    const int col = lane & 15, grp = lane >> 4;
+    const int vk = (key0 + lane / Sh::CPR) * rs2 + 16 * (lane % Sh::CPR);
+#pragma unroll
+    for (int i = 0; i < Sh::KLD; ++i)
+        st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, vk, Sh::RPI * i * rs2, kStreamLoad);
+    const int vv = (key0 + 4 * grp) * rs2 + 2 * Sh::EPL * col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.vB[t][r] = load_vfrag<D>(vr, vv, (16 * t + r) * rs2);
+}
+
+// Consume one step: K rows go through the wave's LDS tile (XOR-swizzled by
+// row so both the row-pattern writes and the MFMA-layout reads are free of
+// bank conflicts), then scores, online softmax and P*V on the matrix cores.
+template <int D, int NT>
+__device__ __forceinline__ void decode_compute_step(const DecodeStepData<D>& st, u32x4* kt, int key0,
+                                                    int end, int lane, float c_log2,
+                                                    const bf16x8 (&qB)[NT][DecodeShape<D>::KI],
+                                                    f32x4 (&O)[NT][DecodeShape<D>::EPL],
+                                                    float (&m_run)[NT], float (&l_run)[NT]) {
+    typedef DecodeShape<D> Sh;
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Sh::KLD; ++i) {
+        const int kl = Sh::RPI * i + lane / Sh::CPR;
+        kt[kl * Sh::CPR + ((lane % Sh::CPR) ^ (kl % Sh::CPR))] = st.kR[i];
+    }
+    u32x4 kA[2][Sh::KI];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < Sh::KI; ++i) {
+            const int kl = 16 * t + col;
+            kA[t][i] = kt[kl * Sh::CPR + ((4 * i + grp) ^ (kl % Sh::CPR))];
+        }
+
+    // V fragments for the P*V product: element 4t+r of lane (col, grp) is
+    // V[key0 + 16t + 4grp + r][EPL*col + e].
+    u32x4 vT[Sh::EPL];
+#pragma unroll
+    for (int e = 0; e < Sh::EPL; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = j >> 1, r = 2 * (j & 1);
+            const uint32_t w0 = st.vB[t][r][e >> 1];
+            const uint32_t w1 = st.vB[t][r + 1][e >> 1];
+            vT[e][j] = (e & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+        }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float p[8];
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < Sh::KI; ++i) acc = mfma16x16x32(as_bf16x8(kA[t][i]), qB[nt][i], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * t + 4 * grp + r;
+                const float sv = key < end ? acc[r] * c_log2 : kNegInf;
+                p[4 * t + r] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[nt], mx);
+        const float alpha = fast_exp2(m_run[nt] - m_new);
+        m_run[nt] = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            p[x] = fast_exp2(p[x] - m_new);
+            psum += p[x];
+        }
+        l_run[nt] = l_run[nt] * alpha + psum;
+
+        // Rescale O: its rows are heads 16nt + 4grp + r, whose alpha sits in lane 4grp + r.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+            for (int e = 0; e < Sh::EPL; ++e) O[nt][e][r] *= ar;
+        }
+
+        u32x4 phi, plo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = __float_as_uint(p[2 * j]);
+            const uint32_t c = __float_as_uint(p[2 * j + 1]);
+            phi[j] = pack_hi16(a, c);
+            const float al = p[2 * j] - __uint_as_float(a & 0xffff0000u);
+            const float cl = p[2 * j + 1] - __uint_as_float(c & 0xffff0000u);
+            plo[j] = pack_bf16x2_rne(al, cl);
+        }
+#pragma unroll
+        for (int e = 0; e < Sh::EPL; ++e) {
+            O[nt][e] = mfma16x16x32(as_bf16x8(phi), as_bf16x8(vT[e]), O[nt][e]);
+            O[nt][e] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vT[e]), O[nt][e]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 split kernel on the matrix cores.
 //
 // Per wave and step of 32 keys (two 16-key sub-tiles t):
+//   loads   K and V rows are streamed with whole-row ("row pattern") loads
+//           that bypass cache allocation; K is rearranged through LDS.
 //   scores  S^T[key][head] = K Q^T with v_mfma_f32_16x16x32_bf16: A = K rows
 //           (lane: key 16t + lane%16, 8 head-dim values), B = the group's
 //           queries (lane: head lane%16, same 8 head-dim values); the 16
@@ -49,10 +190,9 @@ __device__ __forceinline__ typename VFragT<D>::T load_vfrag(const uint16_t* p, b
 //           head lane%16 -- exactly the A-operand layout of the P*V product.
 //   P*V     O[head][dim] += P[head][key] V[key][dim], again 16x16x32 MFMA;
 //           V fragments are 8 keys x 1 head-dim value per lane, built from
-//           row loads (lane: 8 consecutive head-dim values of one key) with
-//           byte permutes.  P is fed as two bf16 terms, hi = truncation of p
-//           and lo = p - hi rounded, so the weights carry ~16 significant
-//           bits and the accumulation is fp32.
+//           the row loads with byte permutes.  P is fed as two bf16 terms,
+//           hi = truncation of p and lo = p - hi rounded, so the weights
+//           carry ~16 significant bits and the accumulation is fp32.
 // NT = number of 16-head tiles (ceil(group size / 16)).
 // ---------------------------------------------------------------------------
 template <int D, int NT>
@@ -61,13 +201,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ seqlens, int Hq, int Hkv,
     int Lmax, int gsize, int S, int chunk, float c_log2, uint16_t* __restrict__ out,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
-    constexpr int KI = D / 32;   // 32-wide slices of the head dim
-    constexpr int EPL = D / 16;  // head-dim values per lane in a V fragment / O
+    typedef DecodeShape<D> Sh;
+    constexpr int KI = Sh::KI;
+    constexpr int EPL = Sh::EPL;
     constexpr int HT = 16 * NT;  // head slots of the workgroup
 
     __shared__ float sm_o[HT * D];
     __shared__ float sm_m[HT];
     __shared__ float sm_l[HT];
+    __shared__ u32x4 k_tiles[kDecodeWaves][32 * Sh::CPR];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -82,9 +224,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
     const int end = min(start + chunk, n);
     if (S > 1 && start >= end) return;  // empty split: the merge skips it
 
-    const int64_t rs = (int64_t)Hkv * D;  // elements between consecutive keys
+    const int rs2 = Hkv * D * 2;  // bytes between consecutive keys of one head
     const uint16_t* kb = kc + ((int64_t)b * Lmax * Hkv + g) * D;
     const uint16_t* vb = vc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const int valid_bytes = end > 0 ? (end - 1) * rs2 + D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, valid_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, valid_bytes);
+    u32x4* kt = k_tiles[wave];
     const int h0 = g * gsize;
 
     bf16x8 qB[NT][KI];
@@ -107,92 +253,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
         for (int e = 0; e < EPL; ++e) O[nt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    typedef typename VFragT<D>::T VT;
     for (int key0 = start + wave * kDecodeStep; key0 < end; key0 += kDecodeWaves * kDecodeStep) {
-        u32x4 kA[2][KI];
-        VT vB[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int key = key0 + 16 * t + col;
-            const uint16_t* kp = kb + (int64_t)key * rs + 8 * grp;
-#pragma unroll
-            for (int i = 0; i < KI; ++i) kA[t][i] = load16(kp + 32 * i, key < end);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 16 * t + 4 * grp + r;
-                vB[t][r] = load_vfrag<D>(vb + (int64_t)key * rs + EPL * col, key < end);
-            }
-
-        // V fragments for the P*V product: element 4t+r of lane (col, grp) is
-        // V[key0 + 16t + 4grp + r][EPL*col + e].
-        u32x4 vT[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = j >> 1, r = 2 * (j & 1);
-                const uint32_t w0 = vB[t][r][e >> 1];
-                const uint32_t w1 = vB[t][r + 1][e >> 1];
-                vT[e][j] = (e & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
-            }
-
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float p[8];
-            float mx = kNegInf;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < KI; ++i) acc = mfma16x16x32(as_bf16x8(kA[t][i]), qB[nt][i], acc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = key0 + 16 * t + 4 * grp + r;
-                    const float sv = key < end ? acc[r] * c_log2 : kNegInf;
-                    p[4 * t + r] = sv;
-                    mx = fmaxf(mx, sv);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[nt], mx);
-            const float alpha = fast_exp2(m_run[nt] - m_new);
-            m_run[nt] = m_new;
-            float psum = 0.f;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                p[x] = fast_exp2(p[x] - m_new);
-                psum += p[x];
-            }
-            l_run[nt] = l_run[nt] * alpha + psum;
-
-            // Rescale O: its rows are heads 16nt + 4grp + r, whose alpha sits in lane 4grp + r.
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) O[nt][e][r] *= ar;
-            }
-
-            u32x4 phi, plo;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t a = __float_as_uint(p[2 * j]);
-                const uint32_t c = __float_as_uint(p[2 * j + 1]);
-                phi[j] = pack_hi16(a, c);
-                const float al = p[2 * j] - __uint_as_float(a & 0xffff0000u);
-                const float cl = p[2 * j + 1] - __uint_as_float(c & 0xffff0000u);
-                plo[j] = pack_bf16x2_rne(al, cl);
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                O[nt][e] = mfma16x16x32(as_bf16x8(phi), as_bf16x8(vT[e]), O[nt][e]);
-                O[nt][e] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vT[e]), O[nt][e]);
-            }
-        }
+        DecodeStepData<D> st;
+        decode_load_step<D>(st, kr, vr, rs2, key0, lane);
+        decode_compute_step<D, NT>(st, kt, key0, end, lane, c_log2, qB, O, m_run, l_run);
     }
 
     // Sum of weights across the four lane groups that share a head.

@@ -17,6 +17,7 @@
 namespace {
 
 constexpr int kMaxGroup = 64;
+constexpr int64_t kMaxChunk = 8192;  // keys per automatic decode piece, at most
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -65,17 +66,17 @@ gqa_status plan_decode(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
     if (num_splits < 0 || num_splits > Lmax) return GQA_ERR_UNSUPPORTED;
     int64_t chunk;
     if (num_splits == 0) {
-        // Aim for about four workgroups per compute unit over the whole
-        // (sequence, KV head, piece) grid, with pieces of 128..2048 keys.
+        // One workgroup per (sequence, KV head) streams the whole cached
+        // length when that already gives every compute unit a workgroup;
+        // otherwise cut the length so it does.  Pieces are capped at
+        // kMaxChunk keys so ragged batches stay balanced.
         int cus = 0;
         st = current_cu_count(&cus);
         if (st != GQA_OK) return st;
-        const int64_t target = 4LL * cus;
         const int64_t pairs = (int64_t)B * Hkv;
-        chunk = cdiv(cdiv((int64_t)Lmax * pairs, target), 128) * 128;
-        if (chunk < 128) chunk = 128;
-        if (chunk > 2048) chunk = 2048;
-        if (chunk > Lmax) chunk = Lmax;
+        int64_t splits = cdiv(cus, pairs);
+        if (splits < cdiv(Lmax, kMaxChunk)) splits = cdiv(Lmax, kMaxChunk);
+        chunk = cdiv(cdiv(Lmax, splits), gqa::kDecodeStep) * gqa::kDecodeStep;
     } else {
         chunk = cdiv(Lmax, num_splits);
     }
