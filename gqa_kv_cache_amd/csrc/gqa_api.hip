@@ -64,6 +64,8 @@ gqa_status plan_decode(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
     if (st != GQA_OK) return st;
     if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
     if (num_splits < 0 || num_splits > Lmax) return GQA_ERR_UNSUPPORTED;
+    // byte offsets inside one sequence's cache slice are 32-bit
+    if ((int64_t)(Lmax + gqa::kDecodeStep) * Hkv * d * 4 > INT_MAX) return GQA_ERR_SHAPE;
     int64_t chunk;
     if (num_splits == 0) {
         // One workgroup per (sequence, KV head) streams the whole cached
@@ -230,6 +232,8 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, int B, int P
     if (st != GQA_OK) return st;
     if (dtype != GQA_BF16) return GQA_ERR_DTYPE;
     if ((int64_t)B * Hq * cdiv(P, gqa::kPrefillRows) > INT_MAX) return GQA_ERR_SHAPE;
+    // byte offsets inside one sequence's K/V are 32-bit
+    if ((int64_t)(P + gqa::kPrefillBN) * Hkv * d * 2 > INT_MAX) return GQA_ERR_SHAPE;
     (void)hipGetLastError();
     if (!gqa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                              static_cast<const uint16_t*>(v), B, P, Hq, Hkv, d, causal != 0,

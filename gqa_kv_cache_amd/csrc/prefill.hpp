@@ -6,14 +6,21 @@
 // "什么减少，什么不减少": the attention multiplications carry no group term).
 //
 // A workgroup owns a block of query rows for `hw` query heads of one group;
-// its four waves share every K and V tile staged in LDS.  Each wave keeps
-// 16*MT query rows of one head in registers and walks the key tiles up to
-// the diagonal with an online softmax (running max m, sum l, unnormalised
-// O).  Scores are formed as S^T = K Q^T so that the result lands directly in
-// the A-operand layout of the P*V product, as in the decode kernel.  V is
-// staged transposed ([head dim][key]) so each lane's P*V operand is 8
-// consecutive keys of one head-dim value.  P is rounded to bf16 for the
-// P*V product; accumulation is fp32.
+// its four waves share every K and V tile staged in LDS (double-buffered:
+// the next tile is loaded into registers while the current one is consumed).
+// Each wave keeps 16*MT query rows of one head in registers and walks the
+// key tiles up to the diagonal with an online softmax (running max m, sum l,
+// unnormalised O).  Scores are formed as S^T = K Q^T so that the result
+// lands directly in the A-operand layout of the P*V product, as in the
+// decode kernel.  V is staged transposed ([head dim][key]) so each lane's
+// P*V operand is 8 consecutive keys of one head-dim value.  P is rounded to
+// bf16 for the P*V product; accumulation is fp32.
+//
+// Softmax reference maximum: the running maximum only moves when a score
+// exceeds it by more than 2^8 (in base-2 units); otherwise the weights are
+// formed against the old maximum and may reach 256, which fp32 sums and bf16
+// weights represent without loss of relative precision.  The final division
+// by the sum of weights makes the result independent of the reference.
 #pragma once
 
 #include "common.hpp"
@@ -22,25 +29,48 @@ namespace gqa {
 
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillBN = 64;  // keys per LDS tile
-constexpr int kPrefillMT = 2;   // 16-row query tiles per wave
+constexpr int kPrefillMT = 4;   // 16-row query tiles per wave
 constexpr int kPrefillRows = 16 * kPrefillMT;  // fewest query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;          // log2 of the largest weight allowed
+
+template <int D> struct PrefillShape {
+    static constexpr int KI = D / 32;    // 32-wide head-dim slices of the score MFMA
+    static constexpr int EPL = D / 16;   // head-dim values per lane in O
+    static constexpr int CPR = D / 8;    // 16-byte chunks per K row
+    static constexpr int KCH = kPrefillBN * CPR / kPrefillThreads;        // K chunks per thread per tile
+    static constexpr int VITEMS = (kPrefillBN / 4) * (D / 8);                  // V 4x8 blocks per tile
+    static constexpr int VCH = (VITEMS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
+};
+
+// Position of 16-byte chunk c of K tile row r: rows read together by one
+// MFMA operand load differ in bits {0,1,3,4} of r, which select the XOR.
+__device__ __forceinline__ int k_slot(int r, int c, int cpr) {
+    return r * cpr + (c ^ ((((r >> 1) & 0xC) | (r & 3)) % cpr));
+}
+// V^T tile: head-dim values d and d^1 share one 256-byte line of 16 chunks
+// (8 keys each); chunk kc of value d sits at slot (8*(d&1) + kc) ^ swizzle.
+__device__ __forceinline__ int v_slot(int d, int kc) {
+    const int line = d >> 1;
+    return line * 16 + ((8 * (d & 1) + kc) ^ ((line >> 2) & 15));
+}
 
 template <int D, int MT>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16(
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, float c_log2,
     uint16_t* __restrict__ out) {
-    constexpr int KI = D / 32;
-    constexpr int EPL = D / 16;
+    typedef PrefillShape<D> Sh;
+    constexpr int KI = Sh::KI;
+    constexpr int EPL = Sh::EPL;
+    constexpr int CPR = Sh::CPR;
     constexpr int WR = 16 * MT;
     constexpr int BN = kPrefillBN;
-    constexpr int KS = D + 8;   // K tile row stride (elements), padded
-    constexpr int VS = BN + 8;  // V^T tile row stride (elements), padded
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VS];
+    __shared__ u32x4 k_lds[2][BN * CPR];
+    __shared__ u32x4 v_lds[2][D * BN / 8];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int col = lane & 15;
     const int grp = lane >> 4;
     // (b, g, head subset) varies fastest; the latest (heaviest) row blocks go first.
@@ -57,11 +87,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16(
     const int iw = i0 + (wave / hw) * WR;
 
     const int64_t qs = (int64_t)Hq * D;
-    const int64_t ks = (int64_t)Hkv * D;
+    const int ks2 = Hkv * D * 2;  // bytes between consecutive positions of one KV head
     const uint16_t* qb = q + (int64_t)b * P * qs + (int64_t)head * D;
-    const uint16_t* kb = k + (int64_t)b * P * ks + (int64_t)g * D;
-    const uint16_t* vb = v + (int64_t)b * P * ks + (int64_t)g * D;
+    const uint16_t* kb = k + (int64_t)b * P * Hkv * D + (int64_t)g * D;
+    const uint16_t* vb = v + (int64_t)b * P * Hkv * D + (int64_t)g * D;
+    const int valid_bytes = (P - 1) * ks2 + D * 2;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, valid_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, valid_bytes, 0x00020000);
 
+    // Query rows of this wave as B operands (lane: row iw + 16mt + col).
     bf16x8 qB[MT][KI];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -72,11 +106,66 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16(
         for (int i = 0; i < KI; ++i) qB[mt][i] = as_bf16x8(load16(qp + 32 * i, ok));
     }
 
+    // Lane-constant LDS slots of the operand reads.
+    int ka_slot[2][KI];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < KI; ++i) ka_slot[t][i] = k_slot(8 * (col >> 2) + 4 * t + (col & 3), 4 * i + grp, CPR);
+    // Chunk kc = 4c + grp of V^T: bit 2 of the unswizzled slot is c, so the
+    // slot for chunk c is the c = 0 slot with bit 2 flipped by c.
+    int vb_slot[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vb_slot[e] = v_slot(EPL * col + e, grp);
+
+    // Tile fill: K as 16-byte chunks, V as blocks of 4 keys x 8 head-dim values.
+    u32x4 kst[Sh::KCH];
+    u32x4 vst[Sh::VCH][4];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int x = 0; x < Sh::KCH; ++x) {
+            const int idx = tid + kPrefillThreads * x;
+            const int r = idx / CPR, cp = idx % CPR;
+            kst[x] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j0 + r) * ks2 + 16 * cp, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < Sh::VCH; ++x) {
+            const int idx = tid + kPrefillThreads * x;
+            if (Sh::VITEMS % kPrefillThreads != 0 && idx >= Sh::VITEMS) break;
+            const int db = idx % (D / 8), k4 = idx / (D / 8);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vst[x][r] = __builtin_amdgcn_raw_buffer_load_b128(vr, (j0 + 4 * k4 + r) * ks2 + 16 * db, 0, 0);
+        }
+    };
+    auto stash = [&](int stage) {
+#pragma unroll
+        for (int x = 0; x < Sh::KCH; ++x) {
+            const int idx = tid + kPrefillThreads * x;
+            k_lds[stage][k_slot(idx / CPR, idx % CPR, CPR)] = kst[x];
+        }
+#pragma unroll
+        for (int x = 0; x < Sh::VCH; ++x) {
+            const int idx = tid + kPrefillThreads * x;
+            if (Sh::VITEMS % kPrefillThreads != 0 && idx >= Sh::VITEMS) break;
+            const int db = idx % (D / 8), k4 = idx / (D / 8);
+            u32x2* vl = reinterpret_cast<u32x2*>(v_lds[stage]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int xw = e >> 1;
+                const uint32_t lo = (e & 1) ? pack_hi16(vst[x][0][xw], vst[x][1][xw]) : pack_lo16(vst[x][0][xw], vst[x][1][xw]);
+                const uint32_t hi = (e & 1) ? pack_hi16(vst[x][2][xw], vst[x][3][xw]) : pack_lo16(vst[x][2][xw], vst[x][3][xw]);
+                // keys 4*k4 .. 4*k4+3 are the (k4 & 1) half of chunk k4 >> 1
+                vl[2 * v_slot(8 * db + e, k4 >> 1) + (k4 & 1)] = u32x2{lo, hi};
+            }
+        }
+    };
+
     f32x4 O[MT][EPL];
-    float m_run[MT], l_run[MT];
+    float m_ref[MT], l_run[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        m_run[mt] = kNegInf;
+        m_ref[mt] = kNegInf;
         l_run[mt] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) O[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -84,102 +173,106 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16(
 
     const int kv_end = causal ? min(P, i0 + rows_wg) : P;
     const int wave_last_row = min(iw + WR, P) - 1;
+    const int ntiles = (kv_end + BN - 1) / BN;
 
-    for (int j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();
-        // K tile, natural layout: 16-byte pieces, 8 head-dim values each.
-        for (int idx = threadIdx.x; idx < BN * (D / 8); idx += kPrefillThreads) {
-            const int r = idx / (D / 8);
-            const int cp = (idx % (D / 8)) * 8;
-            const int key = j0 + r;
-            *reinterpret_cast<u32x4*>(k_lds + r * KS + cp) =
-                load16(kb + (int64_t)(key < P ? key : 0) * ks + cp, key < P);
-        }
-        // V tile, transposed: each thread moves 4 keys x 8 head-dim values.
-        for (int idx = threadIdx.x; idx < (BN / 4) * (D / 8); idx += kPrefillThreads) {
-            const int db = idx % (D / 8);
-            const int k4 = idx / (D / 8);
-            u32x4 w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = j0 + 4 * k4 + r;
-                w[r] = load16(vb + (int64_t)(key < P ? key : 0) * ks + 8 * db, key < P);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int x = e >> 1;
-                const uint32_t lo = (e & 1) ? pack_hi16(w[0][x], w[1][x]) : pack_lo16(w[0][x], w[1][x]);
-                const uint32_t hi = (e & 1) ? pack_hi16(w[2][x], w[3][x]) : pack_lo16(w[2][x], w[3][x]);
-                *reinterpret_cast<u32x2*>(vt_lds + (8 * db + e) * VS + 4 * k4) = u32x2{lo, hi};
-            }
-        }
-        __syncthreads();
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int stage = jt & 1;
+        const int j0 = jt * BN;
+        if (jt + 1 < ntiles) fetch(j0 + BN);
 
-#pragma unroll
+#pragma unroll 1
         for (int c = 0; c < BN / 32; ++c) {
             const int kc0 = j0 + 32 * c;
             if (kc0 >= kv_end) break;
             if (causal && kc0 > wave_last_row) continue;
-            // A operand of S^T = K Q^T: row `col` of sub-tile t is key 8*(col/4) + 4t + col%4.
-            u32x4 kA[2][KI];
+            // chunk keys reach past P or past this wave's first row: mask
+            const bool edge = (kc0 + 31 >= P) || (causal && kc0 + 31 > iw);
+            // S^T = K Q^T for every row tile; each K fragment serves all MT tiles.
+            f32x4 sacc[MT][2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int rt = 32 * c + 8 * (col >> 2) + 4 * t + (col & 3);
+            for (int mt = 0; mt < MT; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < KI; ++i)
-                    kA[t][i] = *reinterpret_cast<const u32x4*>(k_lds + rt * KS + 32 * i + 8 * grp);
-            }
-            // B operand of O += P V: head-dim value EPL*col + e, keys 8*grp .. 8*grp+7.
-            u32x4 vF[EPL];
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                vF[e] = *reinterpret_cast<const u32x4*>(vt_lds + (EPL * col + e) * VS + 32 * c + 8 * grp);
-
+                for (int i = 0; i < KI; ++i) {
+                    const u32x4 kA = k_lds[stage][ka_slot[t][i] + 32 * c * CPR];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int qrow = iw + 16 * mt + col;
-                float p[8];
-                float mx = kNegInf;
+                    for (int mt = 0; mt < MT; ++mt)
+                        sacc[mt][t] = mfma16x16x32(as_bf16x8(kA), qB[mt][i], sacc[mt][t]);
+                }
+            float p[MT][8];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int i = 0; i < KI; ++i) acc = mfma16x16x32(as_bf16x8(kA[t][i]), qB[mt][i], acc);
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = kc0 + 8 * grp + 4 * t + r;
-                        const bool ok = key < P && (!causal || key <= qrow);
-                        const float sv = ok ? acc[r] * c_log2 : kNegInf;
-                        p[4 * t + r] = sv;
-                        mx = fmaxf(mx, sv);
+                    for (int r = 0; r < 4; ++r) p[mt][4 * t + r] = sacc[mt][t][r] * c_log2;
+            if (edge) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int qrow = iw + 16 * mt + col;
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const int key = kc0 + 8 * grp + x;
+                        if (key >= P || (causal && key > qrow)) p[mt][x] = kNegInf;
                     }
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[mt], mx);
-                const float alpha = fast_exp2(m_run[mt] - m_new);
-                m_run[mt] = m_new;
+            }
+            float mx[MT];
+            bool grow = false;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                mx[mt] = p[mt][0];
+#pragma unroll
+                for (int x = 1; x < 8; ++x) mx[mt] = fmaxf(mx[mt], p[mt][x]);
+                grow |= mx[mt] > m_ref[mt] + kRescaleSlack;
+            }
+            // Move the reference maxima only when a weight would exceed 2^slack.
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    float rm = fmaxf(mx[mt], __shfl_xor(mx[mt], 16));
+                    rm = fmaxf(rm, __shfl_xor(rm, 32));
+                    const float m_new = fmaxf(m_ref[mt], rm);
+                    const float alpha = fast_exp2(m_ref[mt] - m_new);
+                    m_ref[mt] = m_new;
+                    l_run[mt] *= alpha;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) O[mt][e][r] *= ar;
+                    }
+                }
+            }
+            u32x4 pa[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float mr = m_ref[mt];
                 float psum = 0.f;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
-                    p[x] = fast_exp2(p[x] - m_new);
-                    psum += p[x];
+                    p[mt][x] = fast_exp2(p[mt][x] - mr);
+                    psum += p[mt][x];
                 }
-                l_run[mt] = l_run[mt] * alpha + psum;
+                l_run[mt] += psum;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float ar = __shfl(alpha, 4 * grp + r);
+                for (int j = 0; j < 4; ++j) pa[mt][j] = pack_bf16x2_rne(p[mt][2 * j], p[mt][2 * j + 1]);
+            }
+            // O += P V; each V fragment serves all MT tiles.
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) O[mt][e][r] *= ar;
-                }
-                u32x4 pa;
+            for (int e = 0; e < EPL; ++e) {
+                const u32x4 vF = v_lds[stage][vb_slot[e] ^ (c << 2)];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pa[j] = pack_bf16x2_rne(p[2 * j], p[2 * j + 1]);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    O[mt][e] = mfma16x16x32(as_bf16x8(pa), as_bf16x8(vF[e]), O[mt][e]);
+                for (int mt = 0; mt < MT; ++mt)
+                    O[mt][e] = mfma16x16x32(as_bf16x8(pa[mt]), as_bf16x8(vF), O[mt][e]);
             }
         }
+        if (jt + 1 < ntiles) stash(stage ^ 1);
+        __syncthreads();
     }
 
 #pragma unroll

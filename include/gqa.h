@@ -78,7 +78,9 @@ const char *gqa_status_str(gqa_status s);
  *   out      [B, Hq, d]
  *   scale    softmax scale, normally 1/sqrt(d)
  *   dtype    GQA_F32 or GQA_BF16
- *   d        64 or 128;  1 <= Hq/Hkv <= 64;  B, Hq, Hkv, Lmax >= 1
+ *   d        64 or 128;  1 <= Hq/Hkv <= 64;  B, Hq, Hkv, Lmax >= 1;
+ *            (Lmax + 32) * Hkv * d * 4 must not exceed 2^31 - 1 (one
+ *            sequence's cache slice is addressed with 32-bit byte offsets)
  *   num_splits  0 = choose automatically; otherwise the number of pieces
  *            the cached length is cut into (1 <= num_splits <= Lmax).  With
  *            more than one piece, partial results (running max, sum of
@@ -118,7 +120,8 @@ gqa_status gqa_decode_workspace_size(int B, int Hq, int Hkv, int d, int Lmax, gq
  *   v    [B, P, Hkv, d]
  *   out  [B, P, Hq, d]
  *   dtype  GQA_BF16 only (the matrix-core path); GQA_F32 -> GQA_ERR_DTYPE
- *   d      64 or 128;  1 <= Hq/Hkv <= 64;  B, P, Hq, Hkv >= 1
+ *   d      64 or 128;  1 <= Hq/Hkv <= 64;  B, P, Hq, Hkv >= 1;
+ *          (P + 64) * Hkv * d * 2 must not exceed 2^31 - 1
  *
  * Returns GQA_OK or an error code; see the conventions above.
  * ------------------------------------------------------------------------ */
