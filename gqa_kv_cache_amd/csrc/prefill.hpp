@@ -27,19 +27,21 @@
 
 namespace gqa {
 
-constexpr int kPrefillThreads = 256;
-constexpr int kPrefillBN = 64;  // keys per LDS tile
-constexpr int kPrefillMT = 4;   // 16-row query tiles per wave
-constexpr int kPrefillRows = 16 * kPrefillMT;  // fewest query rows per workgroup
+constexpr int kPrefillWaves = 8;                    // waves per workgroup (2 per SIMD)
+constexpr int kPrefillBN = 64;                      // keys per LDS tile
+constexpr int kPrefillMT = 2;                       // 16-row query tiles per wave
+constexpr int kPrefillRows = 16 * kPrefillMT * 2;   // fewest query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;          // log2 of the largest weight allowed
 
-template <int D> struct PrefillShape {
+template <int D, int NW, int BN> struct PrefillShape {
+    static constexpr int NTH = 64 * NW;  // threads per workgroup
     static constexpr int KI = D / 32;    // 32-wide head-dim slices of the score MFMA
     static constexpr int EPL = D / 16;   // head-dim values per lane in O
     static constexpr int CPR = D / 8;    // 16-byte chunks per K row
-    static constexpr int KCH = kPrefillBN * CPR / kPrefillThreads;        // K chunks per thread per tile
-    static constexpr int VITEMS = (kPrefillBN / 4) * (D / 8);                  // V 4x8 blocks per tile
-    static constexpr int VCH = (VITEMS + kPrefillThreads - 1) / kPrefillThreads;  // per thread
+    static constexpr int KCH = BN * CPR / NTH;                  // K chunks per thread per tile
+    static_assert(BN * CPR % NTH == 0, "K tile splits evenly over threads");
+    static constexpr int VITEMS = (BN / 4) * (D / 8);           // V 4x8 blocks per tile
+    static constexpr int VCH = (VITEMS + NTH - 1) / NTH;        // per thread
 };
 
 // Position of 16-byte chunk c of K tile row r: rows read together by one
@@ -47,24 +49,31 @@ template <int D> struct PrefillShape {
 __device__ __forceinline__ int k_slot(int r, int c, int cpr) {
     return r * cpr + (c ^ ((((r >> 1) & 0xC) | (r & 3)) % cpr));
 }
-// V^T tile: head-dim values d and d^1 share one 256-byte line of 16 chunks
-// (8 keys each); chunk kc of value d sits at slot (8*(d&1) + kc) ^ swizzle.
+// V^T tile: each head-dim value d holds BN keys as BN/8 chunks of 8 keys;
+// DPL = 16/(BN/8) consecutive values share one 256-byte line of 16 chunks.
+// The XOR spreads the 16 values one MFMA operand load reads (d = 8*lane + e)
+// over distinct chunk positions.
+template <int BN>
 __device__ __forceinline__ int v_slot(int d, int kc) {
-    const int line = d >> 1;
-    return line * 16 + ((8 * (d & 1) + kc) ^ ((line >> 2) & 15));
+    static_assert(BN == 32 || BN == 64 || BN == 128, "key tile of 32, 64 or 128");
+    constexpr int CPD = BN / 8;
+    constexpr int DPL = 16 / CPD;
+    constexpr int SH = DPL == 1 ? 3 : DPL == 2 ? 2 : 1;  // (line >> SH) == d / 8
+    const int line = d / DPL;
+    return line * 16 + ((CPD * (d % DPL) + kc) ^ ((line >> SH) & 15));
 }
 
-template <int D, int MT>
-__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
+template <int D, int MT, int NW, int BN, bool UNROLL>
+__global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, float c_log2,
     uint16_t* __restrict__ out) {
-    typedef PrefillShape<D> Sh;
+    typedef PrefillShape<D, NW, BN> Sh;
     constexpr int KI = Sh::KI;
     constexpr int EPL = Sh::EPL;
     constexpr int CPR = Sh::CPR;
     constexpr int WR = 16 * MT;
-    constexpr int BN = kPrefillBN;
+    constexpr int NTH = Sh::NTH;
     __shared__ u32x4 k_lds[2][BN * CPR];
     __shared__ u32x4 v_lds[2][D * BN / 8];
 
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
     const int bg = bgh / hsets;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
-    const int rows_wg = WR * (4 / hw);
+    const int rows_wg = WR * (NW / hw);
     const int i0 = rb * rows_wg;
     const int head = g * gsize + hs * hw + (wave % hw);
     const int iw = i0 + (wave / hw) * WR;
@@ -103,8 +112,17 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
         const bool ok = row < P;
         const uint16_t* qp = qb + (int64_t)(ok ? row : 0) * qs + 8 * grp;
 #pragma unroll
-        for (int i = 0; i < KI; ++i) qB[mt][i] = as_bf16x8(load16(qp + 32 * i, ok));
+        for (int i = 0; i < KI; ++i) {
+            u32x4 w = load16(qp + 32 * i, ok);
+            // A negative scale is applied as a positive one to -q (exact in bf16).
+            if (c_log2 < 0.f) w ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            qB[mt][i] = as_bf16x8(w);
+        }
     }
+    // |scale| * log2(e), kept away from zero so masked (-inf) scores still
+    // give zero weight; a zero scale then yields equal weights as it should.
+    const float cs = fmaxf(fabsf(c_log2), 1e-30f);
+    const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
     // Lane-constant LDS slots of the operand reads.
     int ka_slot[2][KI];
@@ -112,11 +130,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < KI; ++i) ka_slot[t][i] = k_slot(8 * (col >> 2) + 4 * t + (col & 3), 4 * i + grp, CPR);
-    // Chunk kc = 4c + grp of V^T: bit 2 of the unswizzled slot is c, so the
-    // slot for chunk c is the c = 0 slot with bit 2 flipped by c.
+    // Chunk kc = 4c + grp of V^T: bit 2 of the unswizzled slot is c (64-key
+    // tiles), so the slot for chunk c is the c = 0 slot with bit 2 flipped.
     int vb_slot[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) vb_slot[e] = v_slot(EPL * col + e, grp);
+    for (int e = 0; e < EPL; ++e) vb_slot[e] = v_slot<BN>(EPL * col + e, grp);
 
     // Tile fill: K as 16-byte chunks, V as blocks of 4 keys x 8 head-dim values.
     u32x4 kst[Sh::KCH];
@@ -124,14 +142,14 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int x = 0; x < Sh::KCH; ++x) {
-            const int idx = tid + kPrefillThreads * x;
+            const int idx = tid + NTH * x;
             const int r = idx / CPR, cp = idx % CPR;
             kst[x] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j0 + r) * ks2 + 16 * cp, 0, 0);
         }
 #pragma unroll
         for (int x = 0; x < Sh::VCH; ++x) {
-            const int idx = tid + kPrefillThreads * x;
-            if (Sh::VITEMS % kPrefillThreads != 0 && idx >= Sh::VITEMS) break;
+            const int idx = tid + NTH * x;
+            if (Sh::VITEMS % NTH != 0 && idx >= Sh::VITEMS) break;
             const int db = idx % (D / 8), k4 = idx / (D / 8);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -141,13 +159,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
     auto stash = [&](int stage) {
 #pragma unroll
         for (int x = 0; x < Sh::KCH; ++x) {
-            const int idx = tid + kPrefillThreads * x;
+            const int idx = tid + NTH * x;
             k_lds[stage][k_slot(idx / CPR, idx % CPR, CPR)] = kst[x];
         }
 #pragma unroll
         for (int x = 0; x < Sh::VCH; ++x) {
-            const int idx = tid + kPrefillThreads * x;
-            if (Sh::VITEMS % kPrefillThreads != 0 && idx >= Sh::VITEMS) break;
+            const int idx = tid + NTH * x;
+            if (Sh::VITEMS % NTH != 0 && idx >= Sh::VITEMS) break;
             const int db = idx % (D / 8), k4 = idx / (D / 8);
             u32x2* vl = reinterpret_cast<u32x2*>(v_lds[stage]);
 #pragma unroll
@@ -156,17 +174,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
                 const uint32_t lo = (e & 1) ? pack_hi16(vst[x][0][xw], vst[x][1][xw]) : pack_lo16(vst[x][0][xw], vst[x][1][xw]);
                 const uint32_t hi = (e & 1) ? pack_hi16(vst[x][2][xw], vst[x][3][xw]) : pack_lo16(vst[x][2][xw], vst[x][3][xw]);
                 // keys 4*k4 .. 4*k4+3 are the (k4 & 1) half of chunk k4 >> 1
-                vl[2 * v_slot(8 * db + e, k4 >> 1) + (k4 & 1)] = u32x2{lo, hi};
+                vl[2 * v_slot<BN>(8 * db + e, k4 >> 1) + (k4 & 1)] = u32x2{lo, hi};
             }
         }
     };
 
+    // O accumulators; osum accumulates P times a column of ones, i.e. the sum
+    // of the bf16 weights actually used, per row in the O row layout.
     f32x4 O[MT][EPL];
-    float m_ref[MT], l_run[MT];
+    f32x4 osum[MT];
+    float m_ref[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         m_ref[mt] = kNegInf;
-        l_run[mt] = 0.f;
+        osum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < EPL; ++e) O[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -183,8 +204,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
         const int j0 = jt * BN;
         if (jt + 1 < ntiles) fetch(j0 + BN);
 
-#pragma unroll 1
+#pragma unroll
         for (int c = 0; c < BN / 32; ++c) {
+            if (!UNROLL) __builtin_amdgcn_sched_barrier(0);
             const int kc0 = j0 + 32 * c;
             if (kc0 >= kv_end) break;
             if (causal && kc0 > wave_last_row) continue;
@@ -203,13 +225,14 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
                     for (int mt = 0; mt < MT; ++mt)
                         sacc[mt][t] = mfma16x16x32(as_bf16x8(kA), qB[mt][i], sacc[mt][t]);
                 }
+            // raw scores; masked ones become -inf (weight exp2(-inf) = 0)
             float p[MT][8];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) p[mt][4 * t + r] = sacc[mt][t][r] * c_log2;
+                    for (int r = 0; r < 4; ++r) p[mt][4 * t + r] = sacc[mt][t][r];
             if (edge) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
                 mx[mt] = p[mt][0];
 #pragma unroll
                 for (int x = 1; x < 8; ++x) mx[mt] = fmaxf(mx[mt], p[mt][x]);
-                grow |= mx[mt] > m_ref[mt] + kRescaleSlack;
+                grow |= mx[mt] * cs > m_ref[mt] + kRescaleSlack;
             }
             // Move the reference maxima only when a weight would exceed 2^slack.
             if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -236,13 +259,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
                 for (int mt = 0; mt < MT; ++mt) {
                     float rm = fmaxf(mx[mt], __shfl_xor(mx[mt], 16));
                     rm = fmaxf(rm, __shfl_xor(rm, 32));
-                    const float m_new = fmaxf(m_ref[mt], rm);
+                    const float m_new = fmaxf(m_ref[mt], rm * cs);
                     const float alpha = fast_exp2(m_ref[mt] - m_new);
                     m_ref[mt] = m_new;
-                    l_run[mt] *= alpha;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float ar = __shfl(alpha, 4 * grp + r);
+                        osum[mt][r] *= ar;
 #pragma unroll
                         for (int e = 0; e < EPL; ++e) O[mt][e][r] *= ar;
                     }
@@ -252,15 +275,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const float mr = m_ref[mt];
-                float psum = 0.f;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    p[mt][x] = fast_exp2(p[mt][x] - mr);
-                    psum += p[mt][x];
-                }
-                l_run[mt] += psum;
+                for (int x = 0; x < 8; ++x) p[mt][x] = fast_exp2(__builtin_fmaf(p[mt][x], cs, -mr));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pa[mt][j] = pack_bf16x2_rne(p[mt][2 * j], p[mt][2 * j + 1]);
+                osum[mt] = mfma16x16x32(as_bf16x8(pa[mt]), ones, osum[mt]);
             }
             // O += P V; each V fragment serves all MT tiles.
 #pragma unroll
@@ -277,12 +296,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        l_run[mt] += __shfl_xor(l_run[mt], 16);
-        l_run[mt] += __shfl_xor(l_run[mt], 32);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = iw + 16 * mt + 4 * grp + r;
-            const float l = __shfl(l_run[mt], 4 * grp + r);
+            const float l = osum[mt][r];
             if (row < P) {
                 uint16_t* dst = out + ((int64_t)b * P + row) * qs + (int64_t)head * D + EPL * col;
                 const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -303,23 +320,28 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16(
 }
 
 // Host-side launch; returns false if the launch itself failed.
-inline bool launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
-                           int Hq, int Hkv, int d, bool causal, float c_log2, uint16_t* out,
-                           hipStream_t stream) {
+template <int D, int MT, int NW, int BN, bool UNROLL>
+inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
+                               int Hq, int Hkv, bool causal, float c_log2, uint16_t* out,
+                               hipStream_t stream) {
     const int gsize = Hq / Hkv;
     const int hw = gsize % 4 == 0 ? 4 : gsize % 2 == 0 ? 2 : 1;
-    const int rows_wg = kPrefillRows * (4 / hw);
+    const int rows_wg = 16 * MT * (NW / hw);
     const int nrb = (P + rows_wg - 1) / rows_wg;
     const int nbgh = B * Hkv * (gsize / hw);
     dim3 grid((unsigned)((int64_t)nbgh * nrb));
-    dim3 block(kPrefillThreads);
-    if (d == 128)
-        hipLaunchKernelGGL((prefill_bf16<128, kPrefillMT>), grid, block, 0, stream, q, k, v, P, Hq, Hkv,
-                           gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
-    else
-        hipLaunchKernelGGL((prefill_bf16<64, kPrefillMT>), grid, block, 0, stream, q, k, v, P, Hq, Hkv,
-                           gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
+    dim3 block(64 * NW);
+    hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN, UNROLL>), grid, block, 0, stream, q, k, v, P, Hq,
+                       Hkv, gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
     return hipGetLastError() == hipSuccess;
+}
+
+inline bool launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
+                           int Hq, int Hkv, int d, bool causal, float c_log2, uint16_t* out,
+                           hipStream_t stream) {
+    if (d == 128)
+        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN, false>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN, false>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
 }
 
 }  // namespace gqa
