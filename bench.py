@@ -31,6 +31,48 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "GQA decode: achieved HBM TB/s + µs/step, Hq=64 Hkv=8 d=128 B=32 L=4096"
 
 
+DECODE_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/decode.hpp",
+                  "gqa_kv_cache_amd/csrc/gqa_api.hip")
+PREFILL_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/prefill.hpp",
+                   "gqa_kv_cache_amd/csrc/gqa_api.hip")
+DECODE_PMC = "profiles/decode_bf16_B32_Hq64_Hkv8_d128_L4096.pmc.txt"
+PREFILL_PMC = "profiles/prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal.pmc.txt"
+
+
+def source_digest(paths) -> str:
+    """sha256 over the kernel sources a profile was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(summary_rel, sources):
+    """HBM bytes per launch from a committed FETCH_SIZE/WRITE_SIZE summary.
+
+    The summary records the digest of the kernel sources it was measured on;
+    if those sources have changed since, the figure no longer applies and
+    None is returned.
+    """
+    path = os.path.join(ROOT, summary_rel)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest(sources):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -108,7 +150,7 @@ def bench_decode_case(case, steps, warmup, copies, torch, gqa):
     return res, out
 
 
-def cpu_baseline(case, gpu_out, torch, min_seconds=10.0, max_passes=3):
+def cpu_baseline(case, gpu_out, torch, min_seconds=10.0, max_passes=200):
     """Time the fp64 oracle on the decode workload on the host cores."""
     import numpy as np
     from oracle import counts, reference as orc
@@ -152,13 +194,14 @@ def bench_prefill(steps, warmup, torch, gqa):
     Hkv = c.k.shape[2]
     flops = gqa.prefill_flops(B, P, Hq, d, True)
     mean_ms = sum(per_call) / len(per_call)
-    tflops = flops / (mean_ms * 1e-3) / 1e12
+    tflops = flops / (ev_ms * 1e-3) / 1e12
     return {
         "workload": c.name, "flops": flops, "bytes": gqa.prefill_bytes(B, P, Hq, Hkv, d, gqa.BF16),
         "us_per_call_median": median(per_call) * 1e3, "us_per_call_mean": mean_ms * 1e3,
         "us_per_step_stream": ev_ms * 1e3,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                     "traffic": pmc_traffic(PREFILL_PMC, PREFILL_SOURCES),
                      "kernel": "prefill_bf16"},
     }
 
@@ -194,10 +237,9 @@ def main():
     log("timing decode: %d warm-up + %d steps, %d cache copies" % (args.warmup, args.steps, args.copies))
     res, out = bench_decode_case(case, args.steps, args.warmup, args.copies, torch, gqa)
     torch.cuda.synchronize()
-    ms = res["event_ms"]
+    ms = res["event_ms"]  # average duration per step over the timed region (stream events)
     value = res["bytes"] / (ms * 1e-3) / 1e12
-    call_ms = res["call_ms_mean"]
-    achieved = res["bytes"] / (call_ms * 1e-3) / 1e9
+    achieved = res["bytes"] / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": value,
@@ -221,8 +263,11 @@ def main():
                    "us_per_call_p90": res["call_ms_p90"] * 1e3,
                    "us_per_step_wall": res["wall_ms"] * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gqa_decode call (decode_split_bf16 + decode_merge)"},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": pmc_traffic(DECODE_PMC, DECODE_SOURCES),
+                     "kernel": "decode_split_bf16" if res["splits"] == 1
+                               else "decode_split_bf16 + decode_merge",
+                     "launches_per_step": 1 if res["splits"] == 1 else 2},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the decode workload")
