@@ -15,6 +15,8 @@ FLAGS = [
     # fp32 arithmetic stays on non-packed VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # every symbol must resolve at link time (a missing kernel stub fails the build)
+    "-Wl,-z,defs",
 ]
 
 

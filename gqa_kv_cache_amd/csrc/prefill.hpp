@@ -6,76 +6,98 @@
 // "什么减少，什么不减少": the attention multiplications carry no group term).
 //
 // A workgroup owns a block of query rows for `hw` query heads of one group;
-// its four waves share every K and V tile staged in LDS (double-buffered:
-// the next tile is loaded into registers while the current one is consumed).
-// Each wave keeps 16*MT query rows of one head in registers and walks the
-// key tiles up to the diagonal with an online softmax (running max m, sum l,
-// unnormalised O).  Scores are formed as S^T = K Q^T so that the result
-// lands directly in the A-operand layout of the P*V product, as in the
-// decode kernel.  V is staged transposed ([head dim][key]) so each lane's
-// P*V operand is 8 consecutive keys of one head-dim value.  P is rounded to
-// bf16 for the P*V product; accumulation is fp32.
+// its waves share every K and V tile staged in LDS.  Tiles are
+// double-buffered: the next tile streams from memory straight into LDS
+// (buffer loads with an LDS destination, no registers involved) while the
+// current one is consumed.  Each wave keeps 16*MT query rows of one head as
+// matrix-core operands in registers and walks the key tiles up to the
+// diagonal with an online softmax (reference maximum m, unnormalised O, sum
+// of weights).  Scores are formed as S^T = K Q^T so that the result lands
+// directly in the A-operand layout of the P*V product, as in the decode
+// kernel.  V stays in its natural [key][head dim] layout and is read with
+// the gfx950 LDS transpose read, which hands each lane 4 consecutive keys of
+// one head-dim value: two such reads form the lane's P*V operand.  P is
+// rounded to bf16 for the P*V product; accumulation is fp32.
 //
 // Softmax reference maximum: the running maximum only moves when a score
 // exceeds it by more than 2^8 (in base-2 units); otherwise the weights are
 // formed against the old maximum and may reach 256, which fp32 sums and bf16
-// weights represent without loss of relative precision.  The final division
-// by the sum of weights makes the result independent of the reference.
+// weights represent without loss of relative precision.  The sum of weights
+// is one more matrix-core product (P times a column of ones), so numerator
+// and denominator use the same rounded weights, and the final division makes
+// the result independent of the reference.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace gqa {
 
-constexpr int kPrefillWaves = 8;                    // waves per workgroup (2 per SIMD)
-constexpr int kPrefillBN = 64;                      // keys per LDS tile
-constexpr int kPrefillMT = 2;                       // 16-row query tiles per wave
-constexpr int kPrefillRows = 16 * kPrefillMT * 2;   // fewest query rows per workgroup
-constexpr float kRescaleSlack = 8.0f;          // log2 of the largest weight allowed
+constexpr int kPrefillWaves = 8;                   // waves per workgroup (2 per SIMD)
+constexpr int kPrefillBN = 64;                     // keys per LDS tile
+constexpr int kPrefillMT = 2;                      // 16-row query tiles per wave
+constexpr bool kPrefillPipe = false;               // overlap next scores with current weights
+constexpr int kPrefillRows = 16 * kPrefillMT * 2;  // fewest query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;              // log2 of the largest weight allowed
 
 template <int D, int NW, int BN> struct PrefillShape {
-    static constexpr int NTH = 64 * NW;  // threads per workgroup
-    static constexpr int KI = D / 32;    // 32-wide head-dim slices of the score MFMA
-    static constexpr int EPL = D / 16;   // head-dim values per lane in O
-    static constexpr int CPR = D / 8;    // 16-byte chunks per K row
-    static constexpr int KCH = BN * CPR / NTH;                  // K chunks per thread per tile
-    static_assert(BN * CPR % NTH == 0, "K tile splits evenly over threads");
-    static constexpr int VITEMS = (BN / 4) * (D / 8);           // V 4x8 blocks per tile
-    static constexpr int VCH = (VITEMS + NTH - 1) / NTH;        // per thread
+    static constexpr int KI = D / 32;          // 32-wide head-dim slices of the score MFMA
+    static constexpr int NB = D / 16;          // 16-wide head-dim blocks of O
+    static constexpr int CPR = D / 8;          // 16-byte chunks per K or V row
+    static constexpr int BLK = BN * CPR / 64;  // 1 KB blocks per tile (one direct load each)
+    static constexpr int BPW = BLK / NW;       // blocks per wave per tile
+    static_assert(BLK % NW == 0, "tile blocks split evenly over waves");
 };
 
-// Position of 16-byte chunk c of K tile row r: rows read together by one
-// MFMA operand load differ in bits {0,1,3,4} of r, which select the XOR.
-__device__ __forceinline__ int k_slot(int r, int c, int cpr) {
-    return r * cpr + (c ^ ((((r >> 1) & 0xC) | (r & 3)) % cpr));
+// Position of 16-byte chunk c in K tile row r.  The 16 rows one operand
+// load reads per pass differ in bits {0,1,3,4} of r; the XOR spreads them
+// over all 64 banks: with 256-byte rows (16 chunks) those four bits pick the
+// chunk, with 128-byte rows bit 0 already picks the half of the banks and
+// bits {1,3,4} pick the chunk.  Bit 2 and bits above 4 are ignored, so rows
+// r + 4 and r + 32 share the pattern of row r.
+__device__ __forceinline__ int k_pos(int r, int c, int cpr) {
+    return cpr == 16 ? c ^ (((r >> 1) & 0xC) | (r & 3)) : c ^ (((r >> 2) & 6) | ((r >> 1) & 1));
 }
-// V^T tile: each head-dim value d holds BN keys as BN/8 chunks of 8 keys;
-// DPL = 16/(BN/8) consecutive values share one 256-byte line of 16 chunks.
-// The XOR spreads the 16 values one MFMA operand load reads (d = 8*lane + e)
-// over distinct chunk positions.
-template <int BN>
-__device__ __forceinline__ int v_slot(int d, int kc) {
-    static_assert(BN == 32 || BN == 64 || BN == 128, "key tile of 32, 64 or 128");
-    constexpr int CPD = BN / 8;
-    constexpr int DPL = 16 / CPD;
-    constexpr int SH = DPL == 1 ? 3 : DPL == 2 ? 2 : 1;  // (line >> SH) == d / 8
-    const int line = d / DPL;
-    return line * 16 + ((CPD * (d % DPL) + kc) ^ ((line >> SH) & 15));
+// Position of chunk c in V tile row r.  One transpose read serves 32 lanes
+// per pass: rows 8g + 0..3 and 8g + 8..11.  The XOR with 2(r & 3) spreads
+// the four rows of one lane group over distinct banks; bit 3 of the row then
+// moves the second group onto the other half of the banks (an offset of 128
+// bytes in a 256-byte row, of 32 bytes in a 128-byte row).
+__device__ __forceinline__ int v_pos(int r, int c, int cpr) {
+    return c ^ ((2 * (r & 3)) % cpr) ^ (((r >> 3) & 1) * (cpr == 16 ? 8 : 2));
 }
 
-template <int D, int MT, int NW, int BN, bool UNROLL>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int MT, int NW, int BN, bool PIPE>
 __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, float c_log2,
     uint16_t* __restrict__ out) {
     typedef PrefillShape<D, NW, BN> Sh;
     constexpr int KI = Sh::KI;
-    constexpr int EPL = Sh::EPL;
+    constexpr int NB = Sh::NB;
     constexpr int CPR = Sh::CPR;
     constexpr int WR = 16 * MT;
-    constexpr int NTH = Sh::NTH;
-    __shared__ u32x4 k_lds[2][BN * CPR];
-    __shared__ u32x4 v_lds[2][D * BN / 8];
+    constexpr int CPT = BN / 32;  // 32-key chunks per tile
+    // One array per stage and operand: distinct objects let the compiler
+    // see that reads of one stage never wait for direct loads into the other.
+    __shared__ u32x4 k_lds0[BN * CPR];
+    __shared__ u32x4 k_lds1[BN * CPR];
+    __shared__ u32x4 v_lds0[BN * CPR];
+    __shared__ u32x4 v_lds1[BN * CPR];
+    // Stages are compile-time constants (std::integral_constant).
+    auto k_stage = [&](auto st) -> u32x4* {
+        if constexpr (decltype(st)::value == 0) return k_lds0;
+        else return k_lds1;
+    };
+    auto v_stage = [&](auto st) -> u32x4* {
+        if constexpr (decltype(st)::value == 0) return v_lds0;
+        else return v_lds1;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,9 +122,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const uint16_t* qb = q + (int64_t)b * P * qs + (int64_t)head * D;
     const uint16_t* kb = k + (int64_t)b * P * Hkv * D + (int64_t)g * D;
     const uint16_t* vb = v + (int64_t)b * P * Hkv * D + (int64_t)g * D;
+    // rows at or past P read as zero
     const int valid_bytes = (P - 1) * ks2 + D * 2;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, valid_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, valid_bytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0, valid_bytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0, valid_bytes, 0x00020000);
 
     // Query rows of this wave as B operands (lane: row iw + 16mt + col).
     bf16x8 qB[MT][KI];
@@ -124,64 +147,57 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const float cs = fmaxf(fabsf(c_log2), 1e-30f);
     const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    // Lane-constant LDS slots of the operand reads.
-    int ka_slot[2][KI];
+    // K operand slots.  Row 4 + r of a chunk swizzles like row r (the XOR
+    // ignores bit 2), so sub-tile t = 1 is sub-tile 0 shifted by 4 rows.
+    int ka_slot[KI];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < KI; ++i) {
+        const int r = 8 * (col >> 2) + (col & 3);
+        ka_slot[i] = r * CPR + k_pos(r, 4 * i + grp, CPR);
+    }
+    // V transpose reads: lane (L = lane % 16, grp) names row 8grp + L/4 and
+    // the 8 bytes of head-dims 16e + 4(L%4) .. +3; it receives keys
+    // 8grp + 0..3 (+4 for the second read) of head-dim 16e + L.
+    int vt_byte[NB];
+    {
+        const int L = lane & 15, m = L & 3;
+        const int r = 8 * grp + (L >> 2);
 #pragma unroll
-        for (int i = 0; i < KI; ++i) ka_slot[t][i] = k_slot(8 * (col >> 2) + 4 * t + (col & 3), 4 * i + grp, CPR);
-    // Chunk kc = 4c + grp of V^T: bit 2 of the unswizzled slot is c (64-key
-    // tiles), so the slot for chunk c is the c = 0 slot with bit 2 flipped.
-    int vb_slot[EPL];
+        for (int e = 0; e < NB; ++e)
+            vt_byte[e] = r * CPR * 16 + v_pos(r, 2 * e + (m >> 1), CPR) * 16 + 8 * (m & 1);
+    }
+    // Tile fill: wave w streams 1 KB blocks w, w + NW, ... straight into
+    // LDS; lane l of a block lands in slot 64*block + l, so it fetches the
+    // global chunk that the swizzle places there (both swizzles are XORs, so
+    // position and chunk map onto each other the same way).
+    int k_off[Sh::BPW], v_off[Sh::BPW];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) vb_slot[e] = v_slot<BN>(EPL * col + e, grp);
-
-    // Tile fill: K as 16-byte chunks, V as blocks of 4 keys x 8 head-dim values.
-    u32x4 kst[Sh::KCH];
-    u32x4 vst[Sh::VCH][4];
-    auto fetch = [&](int j0) {
+    for (int x = 0; x < Sh::BPW; ++x) {
+        const int slot = 64 * (wave + NW * x) + lane;
+        const int r = slot / CPR, pos = slot % CPR;
+        k_off[x] = r * ks2 + 16 * k_pos(r, pos, CPR);
+        v_off[x] = r * ks2 + 16 * v_pos(r, pos, CPR);
+    }
+    // The whole byte offset goes in the per-lane operand, so the range check
+    // of the buffer resource zero-fills every row at or past P.
+    auto fill = [&](auto stage, int j0) {
+        u32x4* kl = k_stage(stage);
+        u32x4* vl = v_stage(stage);
+        const int base = j0 * ks2;
 #pragma unroll
-        for (int x = 0; x < Sh::KCH; ++x) {
-            const int idx = tid + NTH * x;
-            const int r = idx / CPR, cp = idx % CPR;
-            kst[x] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j0 + r) * ks2 + 16 * cp, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < Sh::VCH; ++x) {
-            const int idx = tid + NTH * x;
-            if (Sh::VITEMS % NTH != 0 && idx >= Sh::VITEMS) break;
-            const int db = idx % (D / 8), k4 = idx / (D / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vst[x][r] = __builtin_amdgcn_raw_buffer_load_b128(vr, (j0 + 4 * k4 + r) * ks2 + 16 * db, 0, 0);
-        }
-    };
-    auto stash = [&](int stage) {
-#pragma unroll
-        for (int x = 0; x < Sh::KCH; ++x) {
-            const int idx = tid + NTH * x;
-            k_lds[stage][k_slot(idx / CPR, idx % CPR, CPR)] = kst[x];
-        }
-#pragma unroll
-        for (int x = 0; x < Sh::VCH; ++x) {
-            const int idx = tid + NTH * x;
-            if (Sh::VITEMS % NTH != 0 && idx >= Sh::VITEMS) break;
-            const int db = idx % (D / 8), k4 = idx / (D / 8);
-            u32x2* vl = reinterpret_cast<u32x2*>(v_lds[stage]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int xw = e >> 1;
-                const uint32_t lo = (e & 1) ? pack_hi16(vst[x][0][xw], vst[x][1][xw]) : pack_lo16(vst[x][0][xw], vst[x][1][xw]);
-                const uint32_t hi = (e & 1) ? pack_hi16(vst[x][2][xw], vst[x][3][xw]) : pack_lo16(vst[x][2][xw], vst[x][3][xw]);
-                // keys 4*k4 .. 4*k4+3 are the (k4 & 1) half of chunk k4 >> 1
-                vl[2 * v_slot<BN>(8 * db + e, k4 >> 1) + (k4 & 1)] = u32x2{lo, hi};
-            }
+        for (int x = 0; x < Sh::BPW; ++x) {
+            const int blk = wave + NW * x;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)&kl[64 * blk], 16u,
+                                                     (unsigned)(base + k_off[x]), 0u, 0u, 0u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&vl[64 * blk], 16u,
+                                                     (unsigned)(base + v_off[x]), 0u, 0u, 0u);
         }
     };
 
-    // O accumulators; osum accumulates P times a column of ones, i.e. the sum
-    // of the bf16 weights actually used, per row in the O row layout.
-    f32x4 O[MT][EPL];
+    // O accumulators (lane: head-dims 16e + col of rows 16mt + 4grp + r);
+    // osum accumulates P times a column of ones: the sum of the bf16 weights
+    // actually used, per row in the same layout.
+    f32x4 O[MT][NB];
     f32x4 osum[MT];
     float m_ref[MT];
 #pragma unroll
@@ -189,109 +205,177 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         m_ref[mt] = kNegInf;
         osum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) O[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < NB; ++e) O[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+
+    // S^T = K Q^T of chunk c of the staged tile for every row tile; each K
+    // fragment serves all MT tiles.
+    auto scores = [&](auto stage, int c, f32x4 (&sc)[MT][2]) {
+        const u32x4* kl = k_stage(stage);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sc[mt][0] = sc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const u32x4 kA = kl[ka_slot[i] + (32 * c + 4 * t) * CPR];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    sc[mt][t] = mfma16x16x32(as_bf16x8(kA), qB[mt][i], sc[mt][t]);
+            }
+    };
+    // Causal / tail mask of the chunk starting at key kc0.
+    auto mask = [&](int kc0, f32x4 (&sc)[MT][2]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int qrow = iw + 16 * mt + col;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kc0 + 8 * grp + 4 * t + r;
+                    if (key >= P || (causal && key > qrow)) sc[mt][t][r] = kNegInf;
+                }
+        }
+    };
+    // Move the reference maxima only when a weight would exceed 2^slack.
+    // IEEE maximum (NaN-propagating) needs no canonicalisation of the
+    // matrix-core results, so 8 scores take 4 three-input instructions.
+    auto update_max = [&](const f32x4 (&sc)[MT][2]) {
+        float mx[MT];
+        bool grow = false;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[mt][0][0], sc[mt][0][1]), sc[mt][0][2]);
+            const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[mt][0][3], sc[mt][1][0]), sc[mt][1][1]);
+            const float c = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[mt][1][2], sc[mt][1][3]), a);
+            mx[mt] = __builtin_elementwise_maximum(b, c);
+            grow |= mx[mt] * cs > m_ref[mt] + kRescaleSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                float rm = fmaxf(mx[mt], __shfl_xor(mx[mt], 16));
+                rm = fmaxf(rm, __shfl_xor(rm, 32));
+                const float m_new = fmaxf(m_ref[mt], rm * cs);
+                const float alpha = fast_exp2(m_ref[mt] - m_new);
+                m_ref[mt] = m_new;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * grp + r);
+                    osum[mt][r] *= ar;
+#pragma unroll
+                    for (int e = 0; e < NB; ++e) O[mt][e][r] *= ar;
+                }
+            }
+        }
+    };
+    // Weights 2^(s*|c| - m) rounded to bf16, as the A operand of P*V.
+    auto weights = [&](const f32x4 (&sc)[MT][2], u32x4 (&pa)[MT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float mr = m_ref[mt];
+            float w[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[4 * t + r] = fast_exp2(__builtin_fmaf(sc[mt][t][r], cs, -mr));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pa[mt][j] = pack_bf16x2_rne(w[2 * j], w[2 * j + 1]);
+        }
+    };
+    // O += P V and the weight sums; each V fragment serves all MT tiles.
+    auto accumulate = [&](auto stage, int c, const u32x4 (&pa)[MT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) osum[mt] = mfma16x16x32(as_bf16x8(pa[mt]), ones, osum[mt]);
+        const char* vbase = reinterpret_cast<const char*>(v_stage(stage) + 32 * c * CPR);
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + vt_byte[e]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + vt_byte[e] + 4 * CPR * 16));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 vF = u32x4{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                O[mt][e] = mfma16x16x32(as_bf16x8(pa[mt]), as_bf16x8(vF), O[mt][e]);
+        }
+    };
 
     const int kv_end = causal ? min(P, i0 + rows_wg) : P;
     const int wave_last_row = min(iw + WR, P) - 1;
     const int ntiles = (kv_end + BN - 1) / BN;
+    // keys this wave needs: up to kv_end, and up to its last row when causal
+    const int lim = causal ? min(kv_end, wave_last_row + 1) : kv_end;
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int stage = jt & 1;
+    typedef std::integral_constant<int, 0> Stage0;
+    typedef std::integral_constant<int, 1> Stage1;
+    // One key tile: prefetch the next tile into the other stage (released by
+    // every wave at the previous barrier), consume this one, then wait for
+    // this wave's direct loads and meet the other waves.
+    auto tile = [&](auto stage, int jt) {
+        typedef std::integral_constant<int, 1 - decltype(stage)::value> Other;
         const int j0 = jt * BN;
-        if (jt + 1 < ntiles) fetch(j0 + BN);
-
+        if (jt + 1 < ntiles) fill(Other{}, j0 + BN);
+        const bool full = j0 + BN <= lim && j0 + BN <= P && (!causal || j0 + BN - 1 <= iw);
+        if (full) {
+            if (PIPE) {
+                // The scores of chunk c+1 go to the matrix cores while the
+                // weights of chunk c are formed.
+                f32x4 sc[MT][2];
+                scores(stage, 0, sc);
 #pragma unroll
-        for (int c = 0; c < BN / 32; ++c) {
-            if (!UNROLL) __builtin_amdgcn_sched_barrier(0);
-            const int kc0 = j0 + 32 * c;
-            if (kc0 >= kv_end) break;
-            if (causal && kc0 > wave_last_row) continue;
-            // chunk keys reach past P or past this wave's first row: mask
-            const bool edge = (kc0 + 31 >= P) || (causal && kc0 + 31 > iw);
-            // S^T = K Q^T for every row tile; each K fragment serves all MT tiles.
-            f32x4 sacc[MT][2];
+                for (int c = 0; c < CPT; ++c) {
+                    update_max(sc);
+                    f32x4 sn[MT][2];
+                    if (c + 1 < CPT) scores(stage, c + 1, sn);
+                    u32x4 pa[MT];
+                    weights(sc, pa);
+                    accumulate(stage, c, pa);
+                    if (c + 1 < CPT) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < KI; ++i) {
-                    const u32x4 kA = k_lds[stage][ka_slot[t][i] + 32 * c * CPR];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        sacc[mt][t] = mfma16x16x32(as_bf16x8(kA), qB[mt][i], sacc[mt][t]);
-                }
-            // raw scores; masked ones become -inf (weight exp2(-inf) = 0)
-            float p[MT][8];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) p[mt][4 * t + r] = sacc[mt][t][r];
-            if (edge) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int qrow = iw + 16 * mt + col;
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        const int key = kc0 + 8 * grp + x;
-                        if (key >= P || (causal && key > qrow)) p[mt][x] = kNegInf;
+                        for (int mt = 0; mt < MT; ++mt) {
+                            sc[mt][0] = sn[mt][0];
+                            sc[mt][1] = sn[mt][1];
+                        }
                     }
                 }
-            }
-            float mx[MT];
-            bool grow = false;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                mx[mt] = p[mt][0];
-#pragma unroll
-                for (int x = 1; x < 8; ++x) mx[mt] = fmaxf(mx[mt], p[mt][x]);
-                grow |= mx[mt] * cs > m_ref[mt] + kRescaleSlack;
-            }
-            // Move the reference maxima only when a weight would exceed 2^slack.
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    float rm = fmaxf(mx[mt], __shfl_xor(mx[mt], 16));
-                    rm = fmaxf(rm, __shfl_xor(rm, 32));
-                    const float m_new = fmaxf(m_ref[mt], rm * cs);
-                    const float alpha = fast_exp2(m_ref[mt] - m_new);
-                    m_ref[mt] = m_new;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float ar = __shfl(alpha, 4 * grp + r);
-                        osum[mt][r] *= ar;
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e) O[mt][e][r] *= ar;
-                    }
+            } else {
+#pragma unroll 1
+                for (int c = 0; c < CPT; ++c) {
+                    f32x4 sc[MT][2];
+                    scores(stage, c, sc);
+                    update_max(sc);
+                    u32x4 pa[MT];
+                    weights(sc, pa);
+                    accumulate(stage, c, pa);
                 }
             }
-            u32x4 pa[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float mr = m_ref[mt];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) p[mt][x] = fast_exp2(__builtin_fmaf(p[mt][x], cs, -mr));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pa[mt][j] = pack_bf16x2_rne(p[mt][2 * j], p[mt][2 * j + 1]);
-                osum[mt] = mfma16x16x32(as_bf16x8(pa[mt]), ones, osum[mt]);
-            }
-            // O += P V; each V fragment serves all MT tiles.
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const u32x4 vF = v_lds[stage][vb_slot[e] ^ (c << 2)];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    O[mt][e] = mfma16x16x32(as_bf16x8(pa[mt]), as_bf16x8(vF), O[mt][e]);
+        } else {
+            // Diagonal or tail tile: masked chunks, up to the wave's last key.
+#pragma unroll 1
+            for (int c = 0; c < CPT; ++c) {
+                const int kc0 = j0 + 32 * c;
+                if (kc0 >= lim) break;
+                f32x4 sc[MT][2];
+                scores(stage, c, sc);
+                mask(kc0, sc);
+                update_max(sc);
+                u32x4 pa[MT];
+                weights(sc, pa);
+                accumulate(stage, c, pa);
             }
         }
-        if (jt + 1 < ntiles) stash(stage ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
         __syncthreads();
+    };
+
+    fill(Stage0{}, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        tile(Stage0{}, jt);
+        if (jt + 1 < ntiles) tile(Stage1{}, jt + 1);
     }
 
 #pragma unroll
@@ -301,26 +385,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
             const int row = iw + 16 * mt + 4 * grp + r;
             const float l = osum[mt][r];
             if (row < P) {
-                uint16_t* dst = out + ((int64_t)b * P + row) * qs + (int64_t)head * D + EPL * col;
+                // lane holds head-dims 16e + col of the row
+                uint16_t* dst = out + ((int64_t)b * P + row) * qs + (int64_t)head * D + col;
                 const float inv = l > 0.f ? 1.f / l : 0.f;
-                if constexpr (EPL == 8) {
-                    u32x4 o;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2_rne(O[mt][2 * j][r] * inv, O[mt][2 * j + 1][r] * inv);
-                    *reinterpret_cast<u32x4*>(dst) = o;
-                } else {
-                    u32x2 o;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) o[j] = pack_bf16x2_rne(O[mt][2 * j][r] * inv, O[mt][2 * j + 1][r] * inv);
-                    *reinterpret_cast<u32x2*>(dst) = o;
-                }
+                for (int e = 0; e < NB; ++e) dst[16 * e] = (uint16_t)f32_to_bf16_rne(O[mt][e][r] * inv);
             }
         }
     }
 }
 
 // Host-side launch; returns false if the launch itself failed.
-template <int D, int MT, int NW, int BN, bool UNROLL>
+template <int D, int MT, int NW, int BN, bool PIPE>
 inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
                                int Hq, int Hkv, bool causal, float c_log2, uint16_t* out,
                                hipStream_t stream) {
@@ -331,7 +407,7 @@ inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint1
     const int nbgh = B * Hkv * (gsize / hw);
     dim3 grid((unsigned)((int64_t)nbgh * nrb));
     dim3 block(64 * NW);
-    hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN, UNROLL>), grid, block, 0, stream, q, k, v, P, Hq,
+    hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN, PIPE>), grid, block, 0, stream, q, k, v, P, Hq,
                        Hkv, gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
     return hipGetLastError() == hipSuccess;
 }
@@ -340,8 +416,8 @@ inline bool launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int Hq, int Hkv, int d, bool causal, float c_log2, uint16_t* out,
                            hipStream_t stream) {
     if (d == 128)
-        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN, false>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
-    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN, false>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN, kPrefillPipe>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN, kPrefillPipe>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
 }
 
 }  // namespace gqa
