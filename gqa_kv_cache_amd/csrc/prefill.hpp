@@ -37,7 +37,6 @@ namespace gqa {
 constexpr int kPrefillWaves = 8;                   // waves per workgroup (2 per SIMD)
 constexpr int kPrefillBN = 64;                     // keys per LDS tile
 constexpr int kPrefillMT = 2;                      // 16-row query tiles per wave
-constexpr bool kPrefillPipe = false;               // overlap next scores with current weights
 constexpr int kPrefillRows = 16 * kPrefillMT * 2;  // fewest query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;              // log2 of the largest weight allowed
 
@@ -72,7 +71,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int MT, int NW, int BN, bool PIPE>
+template <int D, int MT, int NW, int BN>
 __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, float c_log2,
@@ -90,18 +89,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     __shared__ u32x4 v_lds0[BN * CPR];
     __shared__ u32x4 v_lds1[BN * CPR];
     // Stages are compile-time constants (std::integral_constant).
-    auto k_stage = [&](auto st) -> u32x4* {
+    auto k_stage = [&](auto st) __attribute__((always_inline)) -> u32x4* {
         if constexpr (decltype(st)::value == 0) return k_lds0;
         else return k_lds1;
     };
-    auto v_stage = [&](auto st) -> u32x4* {
+    auto v_stage = [&](auto st) __attribute__((always_inline)) -> u32x4* {
         if constexpr (decltype(st)::value == 0) return v_lds0;
         else return v_lds1;
     };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index as a scalar: everything derived from it is wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
     // (b, g, head subset) varies fastest; the latest (heaviest) row blocks go first.
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     }
     // The whole byte offset goes in the per-lane operand, so the range check
     // of the buffer resource zero-fills every row at or past P.
-    auto fill = [&](auto stage, int j0) {
+    auto fill = [&](auto stage, int j0) __attribute__((always_inline)) {
         u32x4* kl = k_stage(stage);
         u32x4* vl = v_stage(stage);
         const int base = j0 * ks2;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
 
     // S^T = K Q^T of chunk c of the staged tile for every row tile; each K
     // fragment serves all MT tiles.
-    auto scores = [&](auto stage, int c, f32x4 (&sc)[MT][2]) {
+    auto scores = [&](auto stage, int c, f32x4 (&sc)[MT][2]) __attribute__((always_inline)) {
         const u32x4* kl = k_stage(stage);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sc[mt][0] = sc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
             }
     };
     // Causal / tail mask of the chunk starting at key kc0.
-    auto mask = [&](int kc0, f32x4 (&sc)[MT][2]) {
+    auto mask = [&](int kc0, f32x4 (&sc)[MT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int qrow = iw + 16 * mt + col;
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     // Move the reference maxima only when a weight would exceed 2^slack.
     // IEEE maximum (NaN-propagating) needs no canonicalisation of the
     // matrix-core results, so 8 scores take 4 three-input instructions.
-    auto update_max = [&](const f32x4 (&sc)[MT][2]) {
+    auto update_max = [&](const f32x4 (&sc)[MT][2]) __attribute__((always_inline)) {
         float mx[MT];
         bool grow = false;
 #pragma unroll
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         }
     };
     // Weights 2^(s*|c| - m) rounded to bf16, as the A operand of P*V.
-    auto weights = [&](const f32x4 (&sc)[MT][2], u32x4 (&pa)[MT]) {
+    auto weights = [&](const f32x4 (&sc)[MT][2], u32x4 (&pa)[MT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const float mr = m_ref[mt];
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         }
     };
     // O += P V and the weight sums; each V fragment serves all MT tiles.
-    auto accumulate = [&](auto stage, int c, const u32x4 (&pa)[MT]) {
+    auto accumulate = [&](auto stage, int c, const u32x4 (&pa)[MT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) osum[mt] = mfma16x16x32(as_bf16x8(pa[mt]), ones, osum[mt]);
         const char* vbase = reinterpret_cast<const char*>(v_stage(stage) + 32 * c * CPR);
@@ -313,43 +313,20 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     // One key tile: prefetch the next tile into the other stage (released by
     // every wave at the previous barrier), consume this one, then wait for
     // this wave's direct loads and meet the other waves.
-    auto tile = [&](auto stage, int jt) {
+    auto tile = [&](auto stage, int jt) __attribute__((always_inline)) {
         typedef std::integral_constant<int, 1 - decltype(stage)::value> Other;
         const int j0 = jt * BN;
         if (jt + 1 < ntiles) fill(Other{}, j0 + BN);
         const bool full = j0 + BN <= lim && j0 + BN <= P && (!causal || j0 + BN - 1 <= iw);
         if (full) {
-            if (PIPE) {
-                // The scores of chunk c+1 go to the matrix cores while the
-                // weights of chunk c are formed.
-                f32x4 sc[MT][2];
-                scores(stage, 0, sc);
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    update_max(sc);
-                    f32x4 sn[MT][2];
-                    if (c + 1 < CPT) scores(stage, c + 1, sn);
-                    u32x4 pa[MT];
-                    weights(sc, pa);
-                    accumulate(stage, c, pa);
-                    if (c + 1 < CPT) {
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            sc[mt][0] = sn[mt][0];
-                            sc[mt][1] = sn[mt][1];
-                        }
-                    }
-                }
-            } else {
 #pragma unroll 1
-                for (int c = 0; c < CPT; ++c) {
-                    f32x4 sc[MT][2];
-                    scores(stage, c, sc);
-                    update_max(sc);
-                    u32x4 pa[MT];
-                    weights(sc, pa);
-                    accumulate(stage, c, pa);
-                }
+            for (int c = 0; c < CPT; ++c) {
+                f32x4 sc[MT][2];
+                scores(stage, c, sc);
+                update_max(sc);
+                u32x4 pa[MT];
+                weights(sc, pa);
+                accumulate(stage, c, pa);
             }
         } else {
             // Diagonal or tail tile: masked chunks, up to the wave's last key.
@@ -396,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
 }
 
 // Host-side launch; returns false if the launch itself failed.
-template <int D, int MT, int NW, int BN, bool PIPE>
+template <int D, int MT, int NW, int BN>
 inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
                                int Hq, int Hkv, bool causal, float c_log2, uint16_t* out,
                                hipStream_t stream) {
@@ -407,7 +384,7 @@ inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint1
     const int nbgh = B * Hkv * (gsize / hw);
     dim3 grid((unsigned)((int64_t)nbgh * nrb));
     dim3 block(64 * NW);
-    hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN, PIPE>), grid, block, 0, stream, q, k, v, P, Hq,
+    hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN>), grid, block, 0, stream, q, k, v, P, Hq,
                        Hkv, gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
     return hipGetLastError() == hipSuccess;
 }
@@ -416,8 +393,8 @@ inline bool launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int Hq, int Hkv, int d, bool causal, float c_log2, uint16_t* out,
                            hipStream_t stream) {
     if (d == 128)
-        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN, kPrefillPipe>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
-    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN, kPrefillPipe>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
 }
 
 }  // namespace gqa
