@@ -187,3 +187,116 @@ def prefill_causal() -> PrefillCase:
     """Causal prefill: bf16, B=2, P=4096, Hq=32, Hkv=8, d=128."""
     return prefill_case(2, 4096, 32, 8, 128, "bf16", seed=5, causal=True,
                         name="prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal")
+
+
+# --------------------------------------------------------------------------
+# Extended decode inputs (several new tokens, appended rows, FP8 rows, paged
+# pools, windows).  Draws only; the layouts are the ones the extended decode
+# call takes.
+# --------------------------------------------------------------------------
+
+TAG_KNEW, TAG_VNEW, TAG_SCALE, TAG_PERM = 4, 5, 6, 7
+NAN_E4M3 = np.uint8(0x7F)
+
+
+def _draw_e4m3(seed_words, shape) -> np.ndarray:
+    """Random OCP E4M3 codes: random sign and mantissa, exponent field drawn
+    from 3..10 (magnitudes 2^-4 .. 15), so no NaN and no subnormal patterns."""
+    rng = np.random.default_rng(list(seed_words))
+    sign = rng.integers(0, 2, shape, dtype=np.uint8) << np.uint8(7)
+    expo = rng.integers(3, 11, shape, dtype=np.uint8) << np.uint8(3)
+    mant = rng.integers(0, 8, shape, dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
+
+
+@dataclass
+class DecodeExCase:
+    name: str
+    q: np.ndarray            # [B, T, Hq, d]
+    k: np.ndarray            # cache after the append: [B, Lmax, Hkv, d] or pool [nb, bs, Hkv, d]
+    v: np.ndarray
+    k_pre: np.ndarray        # same cache before the append: rows of the new tokens hold NaN
+    v_pre: np.ndarray
+    k_new: np.ndarray        # [B, T, Hkv, d], the rows the append stores
+    v_new: np.ndarray
+    seqlens: np.ndarray      # [B] int32, counts the T new tokens
+    scale: float
+    dtype: str               # q/out dtype: "f32" or "bf16"
+    kv: str                  # "same" (q's dtype) or "fp8"
+    k_scale: np.ndarray = None   # [Hkv] float32 (fp8 only)
+    v_scale: np.ndarray = None
+    block_table: np.ndarray = None   # [B, max_blocks] int32 (paged only)
+    block_size: int = 0
+    window: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def T(self):
+        return self.q.shape[1]
+
+
+def decode_ex_case(B, T, Hq, Hkv, d, Lmax, seqlens, dtype, seed, kv="same", paged=False,
+                   block_size=64, window=0, invalid="nan", scale=None,
+                   name="decode_ex") -> DecodeExCase:
+    """q from [seed, 1]; cached rows of sequence b from [seed, 2|3, b]; the T
+    new rows from [seed, 4|5]; FP8 per-head scales from [seed, 6]; the block
+    permutation of a paged pool from [seed, 7]."""
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    assert seqlens.shape == (B,) and int(seqlens.min()) >= T and int(seqlens.max()) <= Lmax
+    fp8 = kv == "fp8"
+    st = np.uint8 if fp8 else _storage(dtype)
+
+    def rows(words, shape):
+        return _draw_e4m3(words, shape) if fp8 else _draw(words, shape, dtype)
+
+    def poison(a):
+        if fp8:
+            a[...] = NAN_E4M3 if invalid == "nan" else 0
+        else:
+            _fill_invalid(a, dtype, invalid)
+
+    q = _draw([seed, TAG_Q], (B, T, Hq, d), dtype)
+    kc = np.empty((B, Lmax, Hkv, d), st)
+    vc = np.empty((B, Lmax, Hkv, d), st)
+    k_new = rows([seed, TAG_KNEW], (B, T, Hkv, d))
+    v_new = rows([seed, TAG_VNEW], (B, T, Hkv, d))
+    for b in range(B):
+        n = int(seqlens[b])
+        kc[b, :n - T] = rows([seed, TAG_K, b], (n - T, Hkv, d))
+        vc[b, :n - T] = rows([seed, TAG_V, b], (n - T, Hkv, d))
+        poison(kc[b, n - T:])
+        poison(vc[b, n - T:])
+    k_pre, v_pre = kc.copy(), vc.copy()
+    for b in range(B):
+        n = int(seqlens[b])
+        kc[b, n - T:n] = k_new[b]
+        vc[b, n - T:n] = v_new[b]
+
+    k_scale = v_scale = None
+    if fp8:
+        rng = np.random.default_rng([seed, TAG_SCALE])
+        k_scale = rng.uniform(0.05, 0.4, Hkv).astype(np.float32)
+        v_scale = rng.uniform(0.05, 0.4, Hkv).astype(np.float32)
+
+    block_table = None
+    if paged:
+        assert Lmax % block_size == 0
+        maxb = Lmax // block_size
+        nblocks = B * maxb + 3           # a few pool blocks no sequence uses
+        perm = np.random.default_rng([seed, TAG_PERM]).permutation(nblocks)[: B * maxb]
+        block_table = perm.reshape(B, maxb).astype(np.int32)
+
+        def to_pool(c):
+            pool = np.empty((nblocks, block_size, Hkv, d), st)
+            poison(pool)
+            for b in range(B):
+                for i in range(maxb):
+                    pool[block_table[b, i]] = c[b, i * block_size:(i + 1) * block_size]
+            return pool
+
+        kc, vc, k_pre, v_pre = to_pool(kc), to_pool(vc), to_pool(k_pre), to_pool(v_pre)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return DecodeExCase(name, q, kc, vc, k_pre, v_pre, k_new, v_new, seqlens, float(scale), dtype,
+                        kv, k_scale, v_scale, block_table, block_size if paged else 0, int(window),
+                        dict(seed=seed, paged=paged, invalid=invalid))

@@ -69,3 +69,36 @@ def prefill(q, k, v, causal, scale):
             pos_rows.append(head_rows)
         out.append(pos_rows)
     return out
+
+
+def decode_ex(q, k, v, seqlens, scale, window=0, block_table=None, block_size=0):
+    """Several new tokens per sequence, optional window and paged addressing.
+
+    q[B][T][Hq][d].  k/v hold already-widened (and, for FP8 rows, already
+    scaled) values: [B][Lmax][Hkv][d], or a pool [nblocks][block_size][Hkv][d]
+    addressed through block_table[b][j // block_size].  Token t of sequence b
+    is at position seqlens[b] - T + t and sees the keys up to it, the last
+    ``window`` of them when window > 0.
+    """
+    B, T, H = len(q), len(q[0]), len(q[0][0])
+    G = len(k[0][0])
+    out = []
+    for b in range(B):
+        tok_rows = []
+        for t in range(T):
+            pos = seqlens[b] - T + t
+            first = max(0, pos - window + 1) if window > 0 else 0
+            keys = list(range(first, pos + 1))
+            head_rows = []
+            for h1 in range(1, H + 1):
+                g = _group_1indexed(h1, H, G) - 1
+                if block_table is None:
+                    krows = [k[b][j][g] for j in keys]
+                    vrows = [v[b][j][g] for j in keys]
+                else:
+                    krows = [k[block_table[b][j // block_size]][j % block_size][g] for j in keys]
+                    vrows = [v[block_table[b][j // block_size]][j % block_size][g] for j in keys]
+                head_rows.append(_attend(q[b][t][h1 - 1], krows, vrows, scale))
+            tok_rows.append(head_rows)
+        out.append(tok_rows)
+    return out

@@ -359,3 +359,170 @@ int oracle_mqa_decode(const void *q, const void *k, const void *v, const int32_t
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Extended decode: the next rows after the hot path.
+ *
+ *   - Several new query tokens per sequence (speculative verification, the
+ *     multi-token decode step): q [B,T,Hq,d].  seqlens[b] = n counts every
+ *     valid cached row, the T new ones included, so token t sits at position
+ *     pos = n - T + t and attends keys j <= pos: the causal rule of prefill
+ *     ("从MHA到GQA", causal mask section) applied to the new tokens.
+ *   - Sliding window W > 0: only keys j in [pos - W + 1, pos].
+ *   - Cache rows stored as fp32 / bf16 (dtype 0 / 1, like q), or as OCP FP8
+ *     E4M3 bytes (kv_fp8 = 1) whose value is decode(byte) * k_scale[g] for K
+ *     and decode(byte) * v_scale[g] for V, one scale per KV head g.
+ *   - Cache addressing: contiguous [B,Lmax,Hkv,d] (block_table == NULL), or
+ *     paged: row j of sequence b is row j % bs of block
+ *     block_table[b*max_blocks + j / bs] in a pool [nblocks,bs,Hkv,d].
+ * rows == NULL computes all B*T*Hq rows, ordered ((b*T + t)*Hq + h);
+ * otherwise rows[i] names one such index.  Same operation order as
+ * oracle_decode (dot product over c ascending, maximum, exp, sums over j
+ * ascending).  Returns 0 or a negative code.
+ * ------------------------------------------------------------------------ */
+
+/* OCP FP8 E4M3 (the "fn" variant: no infinities): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); the all-ones
+ * pattern S.1111.111 is NaN; the largest finite value is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(unsigned byte)
+{
+    const int sgn = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Element offset of cached row j of sequence b, KV head g. */
+static int64_t orc_row_ex(int64_t b, int64_t j, int64_t g, int64_t Hkv, int64_t d, int64_t Lmax,
+                          const int32_t *block_table, int64_t max_blocks, int64_t bs)
+{
+    if (!block_table)
+        return ((b * Lmax + j) * Hkv + g) * d;
+    const int64_t blk = block_table[b * max_blocks + j / bs];
+    return ((blk * bs + j % bs) * Hkv + g) * d;
+}
+
+static double orc_kv_elem(const void *base, int64_t idx, int dtype, int kv_fp8, double scale)
+{
+    if (kv_fp8)
+        return oracle_e4m3_value(((const uint8_t *)base)[idx]) * scale;
+    return orc_elem(base, idx, dtype);
+}
+
+int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t *seqlens,
+                     int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64_t Lmax,
+                     double scale, int dtype, int kv_fp8, const float *k_scale,
+                     const float *v_scale, const int32_t *block_table, int64_t max_blocks,
+                     int64_t bs, int64_t window, const int64_t *rows, int64_t nrows, double *out)
+{
+    int rc = orc_check_common(B, Hq, Hkv, d, dtype);
+    if (rc)
+        return rc;
+    if (T <= 0 || Lmax < 0 || window < 0)
+        return -1;
+    if (kv_fp8 && (!k_scale || !v_scale))
+        return -1;
+    if (block_table && (bs <= 0 || max_blocks <= 0 || Lmax > max_blocks * bs))
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (seqlens[b] < T || seqlens[b] > Lmax)
+            return -4;
+    if (!rows && nrows != B * T * Hq)
+        return -5;
+    const int64_t gsize = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!w || !acc) {
+#pragma omp atomic write
+            err = -6;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < nrows; ++i) {
+                const int64_t r = rows ? rows[i] : i;
+                if (r < 0 || r >= B * T * Hq) {
+#pragma omp atomic write
+                    err = -5;
+                    continue;
+                }
+                const int64_t h = r % Hq, bt = r / Hq;
+                const int64_t b = bt / T, t = bt % T;
+                const int64_t g = h / gsize; /* contiguous groups */
+                const int64_t pos = seqlens[b] - T + t;
+                const int64_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
+                const int64_t n = pos - lo + 1; /* keys lo .. pos */
+                const double ks = kv_fp8 ? (double)k_scale[g] : 1.0;
+                const double vs = kv_fp8 ? (double)v_scale[g] : 1.0;
+                const int64_t qrow = (bt * Hq + h) * d;
+                double *o = out + i * d;
+                /* scores, j ascending over the visible keys */
+                for (int64_t jj = 0; jj < n; ++jj) {
+                    const int64_t kr = orc_row_ex(b, lo + jj, g, Hkv, d, Lmax, block_table, max_blocks, bs);
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        dot += orc_elem(q, qrow + c, dtype) * orc_kv_elem(k, kr + c, dtype, kv_fp8, ks);
+                    w[jj] = dot * scale;
+                }
+                double m = w[0];
+                for (int64_t jj = 1; jj < n; ++jj)
+                    if (w[jj] > m)
+                        m = w[jj];
+                double z = 0.0;
+                for (int64_t jj = 0; jj < n; ++jj) {
+                    w[jj] = exp(w[jj] - m);
+                    z += w[jj];
+                }
+                for (int64_t c = 0; c < d; ++c)
+                    acc[c] = 0.0;
+                for (int64_t jj = 0; jj < n; ++jj) {
+                    const int64_t vr = orc_row_ex(b, lo + jj, g, Hkv, d, Lmax, block_table, max_blocks, bs);
+                    for (int64_t c = 0; c < d; ++c)
+                        acc[c] += w[jj] * orc_kv_elem(v, vr + c, dtype, kv_fp8, vs);
+                }
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] = acc[c] / z;
+            }
+        }
+        free(w);
+        free(acc);
+    }
+    return err;
+}
+
+/*
+ * Append (Algorithm 2 of "GQA reading notes", the cache-update lines): the T
+ * new K/V rows of sequence b, k_new/v_new [B,T,Hkv,d], are stored at cache
+ * rows seqlens[b] - T + t (seqlens counts them already), contiguous or paged
+ * as in oracle_decode_ex.  elt = bytes per stored element (4 fp32, 2 bf16,
+ * 1 e4m3); the rows are copied byte for byte.
+ */
+int oracle_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                  const int32_t *seqlens, int64_t B, int64_t T, int64_t Hkv, int64_t d,
+                  int64_t Lmax, int64_t elt, const int32_t *block_table, int64_t max_blocks,
+                  int64_t bs)
+{
+    if (B < 0 || T <= 0 || Hkv <= 0 || d <= 0 || Lmax < 0 || (elt != 1 && elt != 2 && elt != 4))
+        return -1;
+    if (block_table && (bs <= 0 || max_blocks <= 0 || Lmax > max_blocks * bs))
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (seqlens[b] < T || seqlens[b] > Lmax)
+            return -4;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t g = 0; g < Hkv; ++g) {
+                const int64_t j = seqlens[b] - T + t;
+                const int64_t dst = orc_row_ex(b, j, g, Hkv, d, Lmax, block_table, max_blocks, bs);
+                const int64_t src = ((b * T + t) * Hkv + g) * d;
+                memcpy((char *)k_cache + dst * elt, (const char *)k_new + src * elt, (size_t)(d * elt));
+                memcpy((char *)v_cache + dst * elt, (const char *)v_new + src * elt, (size_t)(d * elt));
+            }
+    return 0;
+}

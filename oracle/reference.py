@@ -49,6 +49,13 @@ def _bind(lib):
     lib.oracle_mha_decode.restype = ci
     lib.oracle_mqa_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, dbl, ci, vp]
     lib.oracle_mqa_decode.restype = ci
+    lib.oracle_decode_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ci, ci,
+                                     vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.oracle_decode_ex.restype = ci
+    lib.oracle_append.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64]
+    lib.oracle_append.restype = ci
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint]
+    lib.oracle_e4m3_value.restype = dbl
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
     return lib
@@ -200,3 +207,81 @@ def mqa_decode(q, k, v, seqlens, scale) -> np.ndarray:
     if rc:
         raise OracleError("oracle_mqa_decode returned %d" % rc)
     return out
+
+
+def e4m3_value(byte: int) -> float:
+    """Value of one OCP FP8 E4M3 byte (NaN for the S.1111.111 patterns)."""
+    return _load().oracle_e4m3_value(int(byte) & 0xFF)
+
+
+def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_table=None,
+              block_size=0, window=0, rows=None) -> np.ndarray:
+    """Extended GQA decode.  q [B,T,Hq,d] (fp32 or bf16 bits).
+
+    k, v: contiguous [B,Lmax,Hkv,d] or, with ``block_table`` [B,max_blocks],
+    a paged pool [nblocks,block_size,Hkv,d]; stored in q's dtype, or as E4M3
+    bytes (uint8) scaled per KV head by ``k_scale``/``v_scale`` [Hkv].
+    seqlens [B] counts the T new tokens; token t sits at seqlens[b]-T+t.
+    window > 0 keeps the last ``window`` keys of every token.  Returns
+    [B,T,Hq,d] float64, or [len(rows),d] for flat ((b*T+t)*Hq+h) rows.
+    """
+    q, k, v = _c(q), _c(k), _c(v)
+    dt = _dtype_code(q)
+    B, T, Hq, d = q.shape
+    fp8 = k.dtype == np.uint8
+    if fp8:
+        assert v.dtype == np.uint8 and k_scale is not None and v_scale is not None
+    else:
+        assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    assert v.shape == k.shape and k.shape[3] == d
+    Hkv = k.shape[2]
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    assert sl.shape == (B,)
+    if block_table is None:
+        assert k.shape[0] == B
+        Lmax, bt, maxb, bs = k.shape[1], None, 0, 0
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        assert bt.shape[0] == B and k.shape[1] == block_size
+        maxb, bs = bt.shape[1], int(block_size)
+        Lmax = maxb * bs
+        assert bt.min() >= 0 and bt.max() < k.shape[0]
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = None if v_scale is None else np.ascontiguousarray(v_scale, dtype=np.float32)
+    if rows is None:
+        out = np.empty((B, T, Hq, d), np.float64)
+        r, nrows = None, B * T * Hq
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((r.size, d), np.float64)
+        nrows = r.size
+    rc = _load().oracle_decode_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
+                                  B, T, Hq, Hkv, d, Lmax, float(scale), dt, 1 if fp8 else 0,
+                                  _ptr(ks), _ptr(vs), _ptr(bt), maxb, bs, int(window), _ptr(r),
+                                  nrows, out.ctypes.data)
+    if rc:
+        raise OracleError("oracle_decode_ex returned %d" % rc)
+    return out
+
+
+def append(k_cache, v_cache, k_new, v_new, seqlens, *, block_table=None, block_size=0):
+    """Store k_new/v_new [B,T,Hkv,d] at rows seqlens[b]-T+t of the caches, in place.
+
+    The caches are contiguous [B,Lmax,Hkv,d] or paged pools as in decode_ex;
+    rows are copied byte for byte (same element type as the cache).
+    """
+    k_cache, v_cache, k_new, v_new = _c(k_cache), _c(v_cache), _c(k_new), _c(v_new)
+    assert k_cache.dtype == k_new.dtype == v_cache.dtype == v_new.dtype
+    B, T, Hkv, d = k_new.shape
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if block_table is None:
+        Lmax, bt, maxb, bs = k_cache.shape[1], None, 0, 0
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        maxb, bs = bt.shape[1], int(block_size)
+        Lmax = maxb * bs
+    rc = _load().oracle_append(k_cache.ctypes.data, v_cache.ctypes.data, k_new.ctypes.data,
+                               v_new.ctypes.data, sl.ctypes.data, B, T, Hkv, d, Lmax,
+                               k_cache.itemsize, _ptr(bt), maxb, bs)
+    if rc:
+        raise OracleError("oracle_append returned %d" % rc)

@@ -32,6 +32,18 @@ MUTANTS = {
     "v_read_from_k": ("acc[c] += w[j] * orc_elem(v, vr + c, dtype);",
                       "acc[c] += w[j] * orc_elem(k, vr + c, dtype);"),
     "max_not_updated": ("if (w[j] > m)\n            m = w[j];", "if (w[j] > m)\n            m = m;"),
+    "ex_token_order_reversed": ("const int64_t pos = seqlens[b] - T + t;",
+                                "const int64_t pos = seqlens[b] - 1 - t;"),
+    "ex_window_off_by_one": ("(window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;",
+                             "(window > 0 && pos - window > 0) ? pos - window : 0;"),
+    "ex_paged_block_index": ("block_table[b * max_blocks + j / bs];",
+                             "block_table[b * max_blocks + j % bs];"),
+    "ex_e4m3_exponent_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                              "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "ex_v_scale_from_k": ("const double vs = kv_fp8 ? (double)v_scale[g] : 1.0;",
+                          "const double vs = kv_fp8 ? (double)k_scale[g] : 1.0;"),
+    "ex_append_row_off_by_one": ("const int64_t j = seqlens[b] - T + t;",
+                                 "const int64_t j = seqlens[b] - T + t - 1;"),
     "query_row_of_wrong_head": ("orc_attend(q, (b * Hq + h) * d, k, v, ((b * Lmax) * Hkv + g) * d,\n",
                                 "orc_attend(q, (b * Hq + g) * d, k, v, ((b * Lmax) * Hkv + g) * d,\n"),
 }
@@ -67,6 +79,43 @@ def _pins():
         if not np.array_equal(out[0, h], widen(s.v[0, 0, h // 2])):
             failed.append("single_key")
             break
+
+    # extended decode: brute force with every feature on, prefill rows, append
+    import torch
+    e = gi.decode_ex_case(2, 3, 4, 2, 8, 12, [12, 6], "bf16", seed=31, kv="fp8", paged=True,
+                          block_size=4, window=4)
+    try:
+        got = orc.decode_ex(e.q, e.k, e.v, e.seqlens, e.scale, k_scale=e.k_scale,
+                            v_scale=e.v_scale, block_table=e.block_table,
+                            block_size=e.block_size, window=4)
+
+        def w8(codes, sc):
+            t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+            return t.to(torch.float64).numpy() * np.asarray(sc, np.float64)[:, None]
+
+        ref = brute.decode_ex(widen(e.q).tolist(), w8(e.k, e.k_scale).tolist(),
+                              w8(e.v, e.v_scale).tolist(), e.seqlens.tolist(), e.scale, window=4,
+                              block_table=e.block_table.tolist(), block_size=4)
+        if not np.allclose(got, np.array(ref), rtol=1e-12, atol=1e-12):
+            failed.append("brute_decode_ex")
+    except orc.OracleError:
+        failed.append("brute_decode_ex_error")
+    pf = gi.prefill_case(1, 9, 4, 2, 8, "bf16", seed=32)
+    try:
+        rows = orc.decode_ex(np.ascontiguousarray(pf.q[:, 6:]), pf.k, pf.v, np.array([9], np.int32),
+                             pf.scale)
+        if not np.array_equal(rows, orc.prefill(pf.q, pf.k, pf.v, True, pf.scale)[:, 6:]):
+            failed.append("decode_ex_prefill_rows")
+    except orc.OracleError:
+        failed.append("decode_ex_prefill_rows_error")
+    a = gi.decode_ex_case(2, 2, 4, 2, 8, 8, [8, 5], "bf16", seed=33, paged=True, block_size=4)
+    kk, vv2 = a.k_pre.copy(), a.v_pre.copy()
+    try:
+        orc.append(kk, vv2, a.k_new, a.v_new, a.seqlens, block_table=a.block_table, block_size=4)
+        if not (np.array_equal(kk, a.k) and np.array_equal(vv2, a.v)):
+            failed.append("append_rows")
+    except orc.OracleError:
+        failed.append("append_error")
 
     u = gi.decode_case(1, 2, 1, 8, 6, [6], "f32", q_seed=12, kv_seed=13)
     out = orc.decode(u.q, u.k, u.v, u.seqlens, 0.0)
