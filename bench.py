@@ -150,6 +150,54 @@ def bench_decode_case(case, steps, warmup, copies, torch, gqa):
     return res, out
 
 
+def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
+    """Time gqa_decode_ex (no append) over rotated cache copies; returns a result dict."""
+    def dev(a):
+        if a.dtype.name == "uint8":
+            return torch.from_numpy(a).cuda()
+        return to_dev(a, torch)
+
+    cache_bytes = case.k.nbytes + case.v.nbytes
+    copies = max(2, min(8, math.ceil(min_total_bytes / cache_bytes)))
+    q = to_dev(case.q, torch)
+    ks = [dev(case.k)]
+    vs = [dev(case.v)]
+    for _ in range(copies - 1):
+        ks.append(ks[0].clone())
+        vs.append(vs[0].clone())
+    sl = torch.from_numpy(case.seqlens).cuda()
+    kw = {}
+    if case.kv == "fp8":
+        kw["k_scale"] = torch.from_numpy(case.k_scale).cuda()
+        kw["v_scale"] = torch.from_numpy(case.v_scale).cuda()
+    if case.block_table is not None:
+        kw["block_table"] = torch.from_numpy(case.block_table).cuda()
+        kw["block_size"] = case.block_size
+    out = torch.empty_like(q)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+
+    def fn(i):
+        gqa.decode_ex(q, ks[i], vs[i], sl, scale=case.scale, window=case.window, out=out,
+                      workspace=ws, **kw)
+
+    wall_ms, ev_ms, per_call = time_calls(fn, steps, warmup, torch, rotate=copies)
+    B, T, Hq, d = case.q.shape
+    Hkv = case.k.shape[2]
+    elt = 1 if case.kv == "fp8" else 2
+    # rows some token of the sequence can see, read once per KV head; q and out
+    first = [max(0, int(n) - T - case.window + 1) if case.window > 0 else 0 for n in case.seqlens]
+    rows = sum(int(n) - f for n, f in zip(case.seqlens, first))
+    nbytes = rows * 2 * Hkv * d * elt + 2 * B * T * Hq * d * 2
+    us = ev_ms * 1e3
+    del ks, vs
+    return {"workload": case.name, "T": T, "kv_dtype": "e4m3" if case.kv == "fp8" else "bf16",
+            "paged_block_size": case.block_size or None, "window": case.window or None,
+            "bytes": nbytes, "us_per_step": us, "us_per_call_median": median(per_call) * 1e3,
+            "achieved_TBps": nbytes / (us * 1e-6) / 1e12,
+            "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "new_tokens_per_s": B * T / (us * 1e-6), "cache_copies_rotated": copies}
+
+
 def cpu_baseline(case, gpu_out, torch, min_seconds=10.0, max_passes=200):
     """Time the fp64 oracle on the decode workload on the host cores."""
     import numpy as np
@@ -216,6 +264,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--ragged", action="store_true", help="also time the ragged batch (8 GiB cache)")
+    ap.add_argument("--no-extended", action="store_true",
+                    help="skip the extended decode (FP8, several tokens, paged, window)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -294,6 +344,24 @@ def main():
                           "fp32_vector_alu_time_us": fl_alu_us})
             del o
         line["sweep"] = sweep
+    if not args.no_extended:
+        ext = []
+        L70 = dict(B=32, T=1, Hq=64, Hkv=8, d=128, Lmax=4096, seqlens=[4096] * 32, dtype="bf16",
+                   invalid="zero")
+        variants = [
+            ("decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096", dict(kv="fp8")),
+            ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4)),
+            ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64)),
+            ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),
+        ]
+        for name, extra in variants:
+            log("timing %s" % name)
+            a = dict(L70)
+            a.update(extra)
+            c = gi.decode_ex_case(seed=60, name=name, **a)
+            ext.append(bench_decode_ex(c, max(20, args.steps // 2), args.warmup, torch, gqa))
+            del c
+        line["extended"] = ext
     if args.ragged:
         log("generating the ragged workload (8 GiB cache)")
         c = gi.ragged_decode(invalid="zero")

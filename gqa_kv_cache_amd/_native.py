@@ -16,7 +16,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libgqa.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 
 
 class Status(enum.IntEnum):
@@ -44,8 +44,25 @@ _lib = None
 EXPORTS = (
     "gqa_status_str", "gqa_decode", "gqa_decode_num_splits", "gqa_decode_workspace_size",
     "gqa_prefill", "gqa_kv_cache_elems", "gqa_decode_bytes", "gqa_decode_flops",
-    "gqa_prefill_flops", "gqa_prefill_bytes",
+    "gqa_prefill_flops", "gqa_prefill_bytes", "gqa_decode_ex", "gqa_decode_ex_workspace_size",
 )
+
+
+class DecodeExArgs(ctypes.Structure):
+    """Mirror of gqa_decode_ex_args (include/gqa.h), field for field."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("seqlens", ctypes.c_void_p),
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+        ("d", ctypes.c_int), ("Lmax", ctypes.c_int),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("block_size", ctypes.c_int), ("max_blocks", ctypes.c_int), ("num_blocks", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_splits", ctypes.c_int),
+    ]
 
 
 def load():
@@ -78,6 +95,10 @@ def load():
     lib.gqa_prefill_flops.restype = u64
     lib.gqa_prefill_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.gqa_prefill_bytes.restype = u64
+    lib.gqa_decode_ex.argtypes = [ctypes.POINTER(DecodeExArgs), vp]
+    lib.gqa_decode_ex.restype = ci
+    lib.gqa_decode_ex_workspace_size.argtypes = [ctypes.POINTER(DecodeExArgs), ctypes.POINTER(sz)]
+    lib.gqa_decode_ex_workspace_size.restype = ci
     _lib = lib
     return lib
 
@@ -163,6 +184,103 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, wor
                             B, Hq, Hkv, d, Lmax, float(scale), dt, out.data_ptr(), ws_ptr, ws_bytes,
                             int(num_splits), stream)
     _check(st, "gqa_decode")
+    return out
+
+
+def _kv_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return FP8_E4M3
+    raise TypeError("gqa: KV cache must be bfloat16, or E4M3 bytes (uint8 / float8_e4m3fn)")
+
+
+def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale=None,
+              block_table=None, block_size=0, window=0, k_new=None, v_new=None, out=None,
+              num_splits=0, workspace=None):
+    """Extended decode step (gqa_decode_ex).
+
+    q [B,T,Hq,d] bfloat16; seqlens [B] int32 counts the T new tokens.
+    k_cache, v_cache: contiguous [B,Lmax,Hkv,d] or, with ``block_table``
+    [B,max_blocks] int32, a pool [num_blocks,block_size,Hkv,d]; bfloat16 or
+    E4M3 bytes (uint8 / float8_e4m3fn) with ``k_scale``, ``v_scale`` [Hkv]
+    float32.  ``k_new``/``v_new`` [B,T,Hkv,d] (cache dtype) are stored into the
+    cache first when given.  ``window`` > 0 keeps the last ``window`` keys of
+    each token.  Returns ``out`` [B,T,Hq,d] bfloat16.
+    """
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens)):
+        _require_cuda(name, t)
+    if seqlens.dtype != torch.int32:
+        raise TypeError("gqa: seqlens must be int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("gqa: expected q [B,T,Hq,d] and 4-d caches")
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != d or tuple(seqlens.shape) != (B,):
+        raise ValueError("gqa: inconsistent shapes")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("gqa: q must be bfloat16")
+    kv = _kv_code(k_cache)
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("gqa: k_cache and v_cache must share one dtype")
+    a = DecodeExArgs()
+    if block_table is None:
+        if k_cache.shape[0] != B:
+            raise ValueError("gqa: contiguous caches are [B,Lmax,Hkv,d]")
+        Lmax, max_blocks, num_blocks = k_cache.shape[1], 0, 0
+    else:
+        _require_cuda("block_table", block_table)
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("gqa: block_table must be int32 [B,max_blocks]")
+        if k_cache.shape[1] != block_size:
+            raise ValueError("gqa: paged caches are [num_blocks,block_size,Hkv,d]")
+        max_blocks, num_blocks = block_table.shape[1], k_cache.shape[0]
+        Lmax = max_blocks * block_size
+        a.block_table = block_table.data_ptr()
+    if kv == FP8_E4M3:
+        if k_scale is None or v_scale is None:
+            raise ValueError("gqa: FP8 caches need k_scale and v_scale")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _require_cuda(name, t)
+            if t.dtype != torch.float32 or tuple(t.shape) != (Hkv,):
+                raise ValueError("gqa: %s must be float32 [Hkv]" % name)
+        a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    if (k_new is None) != (v_new is None):
+        raise ValueError("gqa: give both k_new and v_new, or neither")
+    if k_new is not None:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _require_cuda(name, t)
+            if tuple(t.shape) != (B, T, Hkv, d) or t.dtype != k_cache.dtype:
+                raise ValueError("gqa: %s must be [B,T,Hkv,d] in the cache dtype" % name)
+        a.k_new, a.v_new = k_new.data_ptr(), v_new.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_cuda("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("gqa: out must match q in shape and dtype")
+    a.q, a.k_cache, a.v_cache, a.seqlens = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr()
+    a.B, a.T, a.Hq, a.Hkv, a.d, a.Lmax = B, T, Hq, Hkv, d, Lmax
+    a.scale, a.dtype, a.kv_dtype = float(scale), BF16, kv
+    a.block_size, a.max_blocks, a.num_blocks = int(block_size), max_blocks, num_blocks
+    a.window, a.out, a.num_splits = int(window), out.data_ptr(), int(num_splits)
+    with torch.cuda.device(q.device):
+        need = ctypes.c_size_t(0)
+        _check(lib.gqa_decode_ex_workspace_size(ctypes.byref(a), ctypes.byref(need)),
+               "gqa_decode_ex_workspace_size")
+        if need.value:
+            if workspace is None:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+            _require_cuda("workspace", workspace)
+            a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib.gqa_decode_ex(ctypes.byref(a), stream)
+    _check(st, "gqa_decode_ex")
     return out
 
 

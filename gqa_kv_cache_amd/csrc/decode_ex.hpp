@@ -1,0 +1,481 @@
+// Extended GQA decode for gfx950: several new query tokens per sequence, an
+// optional sliding window, a paged cache and an FP8 (OCP E4M3) cache.
+//
+// Same structure as the plain decode kernel (one workgroup per sequence, KV
+// head and split; whole-row loads; K rearranged through a per-wave LDS tile;
+// scores and P*V on v_mfma_f32_16x16x32_bf16), generalised:
+//   - The workgroup's query rows are (token, head) pairs of the group, row
+//     r = t * gsize + h', up to 64 of them.  Token t of a sequence with n
+//     valid rows sits at position n - T + t and sees keys
+//     [max(0, pos - W + 1), pos] (W = window, 0 = all): causal among the new
+//     tokens as in prefill ("从MHA到GQA", causal mask section), restricted to
+//     a window when one is given.
+//   - Every 32-key step of a wave gets its own buffer resource based at the
+//     step's first row: in a paged cache that row lives in block
+//     block_table[b][key0 / block_size] (block_size a multiple of 32, so a
+//     step never crosses a block).  The resource's size ends at the last
+//     valid row, so rows at or past the split end read as zero.
+//   - FP8 rows are converted to bf16 (exact: every E4M3 value is a bf16
+//     value) when K is staged in LDS and when the V fragments are built.  The
+//     per-KV-head scales never touch the elements: k_scale multiplies the
+//     score factor and v_scale the output.
+// Splits write (m, l, acc) like the plain kernel; decode_ex_merge combines
+// the splits that intersect the keys any token of the sequence can see.
+#pragma once
+
+#include "common.hpp"
+#include "decode.hpp"
+
+namespace gqa {
+
+// Byte-level geometry of one cached row.
+template <int D, bool KV8> struct ExShape {
+    static constexpr int ELT = KV8 ? 1 : 2;            // bytes per stored element
+    static constexpr int ROWB = D * ELT;               // bytes per row of one KV head
+    static constexpr int CPR = ROWB / 16;              // 16-byte chunks per stored row
+    static constexpr int RPI = 64 / CPR;               // rows per whole-row K load
+    static constexpr int KLD = 32 / RPI;               // K loads per 32-key step
+    static constexpr int VB = DecodeShape<D>::EPL * ELT;  // bytes of one lane's V piece per row
+};
+
+// Raw V piece of one row for one lane: EPL elements.
+template <int D, bool KV8> struct ExVRaw;
+template <> struct ExVRaw<128, false> { typedef u32x4 T; };
+template <> struct ExVRaw<64, false> { typedef u32x2 T; };
+template <> struct ExVRaw<128, true> { typedef u32x2 T; };
+template <> struct ExVRaw<64, true> { typedef uint32_t T; };
+
+template <int D, bool KV8>
+__device__ __forceinline__ typename ExVRaw<D, KV8>::T ex_load_v(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (ExShape<D, KV8>::VB == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamLoad);
+    else if constexpr (ExShape<D, KV8>::VB == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamLoad);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamLoad);
+}
+
+// Two E4M3 bytes (low or high half of a word) -> two bf16 in one word.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// V piece as bf16 words (the plain kernel's VFragT layout).
+template <int D, bool KV8>
+__device__ __forceinline__ typename VFragT<D>::T ex_v_bf16(typename ExVRaw<D, KV8>::T x) {
+    if constexpr (!KV8) {
+        return x;
+    } else if constexpr (D == 128) {
+        return u32x4{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
+                     e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
+    } else {
+        return u32x2{e4m3x2_to_bf16x2<false>(x), e4m3x2_to_bf16x2<true>(x)};
+    }
+}
+
+template <int D, bool KV8> struct ExStepData {
+    u32x4 kR[ExShape<D, KV8>::KLD];
+    typename ExVRaw<D, KV8>::T vB[2][4];
+};
+
+// Loads of one 32-key step; offsets are relative to the step's first row.
+template <int D, bool KV8>
+__device__ __forceinline__ void ex_load_step(ExStepData<D, KV8>& st, __amdgpu_buffer_rsrc_t kr,
+                                             __amdgpu_buffer_rsrc_t vr, int rs, int lane) {
+    typedef ExShape<D, KV8> Sh;
+    const int col = lane & 15, grp = lane >> 4;
+    const int vk = (lane / Sh::CPR) * rs + 16 * (lane % Sh::CPR);
+#pragma unroll
+    for (int i = 0; i < Sh::KLD; ++i)
+        st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, vk, Sh::RPI * i * rs, kStreamLoad);
+    const int vv = 4 * grp * rs + Sh::VB * col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.vB[t][r] = ex_load_v<D, KV8>(vr, vv, (16 * t + r) * rs);
+}
+
+// K rows into the wave's LDS tile as bf16, in the plain kernel's swizzled
+// layout (row kl, 16-byte bf16 chunk c at kl*CPR + (c ^ (kl % CPR))).
+template <int D, bool KV8>
+__device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV8>& st, u32x4* kt, int lane) {
+    typedef ExShape<D, KV8> Sh;
+    constexpr int CPR16 = DecodeShape<D>::CPR;  // bf16 chunks per row
+#pragma unroll
+    for (int i = 0; i < Sh::KLD; ++i) {
+        const int kl = Sh::RPI * i + lane / Sh::CPR;
+        const int c = lane % Sh::CPR;
+        if constexpr (!KV8) {
+            kt[kl * CPR16 + (c ^ (kl % CPR16))] = st.kR[i];
+        } else {
+            // 16 E4M3 values = head dims 16c .. 16c+15 = bf16 chunks 2c, 2c+1
+            const u32x4 w = st.kR[i];
+            const u32x4 lo = u32x4{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
+                                   e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
+            const u32x4 hi = u32x4{e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
+                                   e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
+            kt[kl * CPR16 + ((2 * c) ^ (kl % CPR16))] = lo;
+            kt[kl * CPR16 + ((2 * c + 1) ^ (kl % CPR16))] = hi;
+        }
+    }
+}
+
+// Scores, masked online softmax and P*V of one step.  lo/hi: inclusive key
+// range of each lane's query row (per 16-row tile); end: split end.
+template <int D, int NT, bool KV8>
+__device__ __forceinline__ void ex_compute_step(const ExStepData<D, KV8>& st, const u32x4* kt,
+                                                int key0, int end, int lane, float c_log2,
+                                                const int (&lo)[NT], const int (&hi)[NT],
+                                                const bf16x8 (&qB)[NT][DecodeShape<D>::KI],
+                                                f32x4 (&O)[NT][DecodeShape<D>::EPL],
+                                                float (&m_run)[NT], float (&l_run)[NT]) {
+    typedef DecodeShape<D> Sh;
+    const int col = lane & 15, grp = lane >> 4;
+    u32x4 kA[2][Sh::KI];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < Sh::KI; ++i) {
+            const int kl = 16 * t + col;
+            kA[t][i] = kt[kl * Sh::CPR + ((4 * i + grp) ^ (kl % Sh::CPR))];
+        }
+    typename VFragT<D>::T vB[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vB[t][r] = ex_v_bf16<D, KV8>(st.vB[t][r]);
+    // element 4t+r of lane (col, grp): V[key0 + 16t + 4grp + r][EPL*col + e]
+    u32x4 vT[Sh::EPL];
+#pragma unroll
+    for (int e = 0; e < Sh::EPL; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = j >> 1, r = 2 * (j & 1);
+            const uint32_t w0 = vB[t][r][e >> 1];
+            const uint32_t w1 = vB[t][r + 1][e >> 1];
+            vT[e][j] = (e & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+        }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float p[8];
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < Sh::KI; ++i) acc = mfma16x16x32(as_bf16x8(kA[t][i]), qB[nt][i], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * t + 4 * grp + r;
+                const bool vis = key < end && key >= lo[nt] && key <= hi[nt];
+                const float sv = vis ? acc[r] * c_log2 : kNegInf;
+                p[4 * t + r] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[nt], mx);
+        // a row that has seen no visible key yet keeps m = -inf; subtract 0
+        // instead so its weights are 0 rather than NaN
+        const float m_sub = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[nt] - m_sub);
+        m_run[nt] = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            p[x] = fast_exp2(p[x] - m_sub);
+            psum += p[x];
+        }
+        l_run[nt] = l_run[nt] * alpha + psum;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+            for (int e = 0; e < Sh::EPL; ++e) O[nt][e][r] *= ar;
+        }
+        // weights as hi + lo bf16 terms (~16 significant bits), as in the plain kernel
+        u32x4 phi, plo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = __float_as_uint(p[2 * j]);
+            const uint32_t c = __float_as_uint(p[2 * j + 1]);
+            phi[j] = pack_hi16(a, c);
+            const float al = p[2 * j] - __uint_as_float(a & 0xffff0000u);
+            const float cl = p[2 * j + 1] - __uint_as_float(c & 0xffff0000u);
+            plo[j] = pack_bf16x2_rne(al, cl);
+        }
+#pragma unroll
+        for (int e = 0; e < Sh::EPL; ++e) {
+            O[nt][e] = mfma16x16x32(as_bf16x8(phi), as_bf16x8(vT[e]), O[nt][e]);
+            O[nt][e] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vT[e]), O[nt][e]);
+        }
+    }
+}
+
+// First key any token of a sequence with n rows can see (window W, T tokens).
+__device__ __forceinline__ int ex_first_key(int n, int T, int window) {
+    return window > 0 ? max(0, n - T - window + 1) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel.  q [B,T,Hq,d] bf16; caches contiguous [B,Lmax,Hkv,d] or a
+// paged pool [nblocks,bs,Hkv,d] (bf16 or E4M3 bytes); out [B,T,Hq,d] bf16.
+// NT = ceil(T * gsize / 16) tiles of 16 query rows; NWV waves per workgroup
+// take the split's 32-key steps in turn.
+// ---------------------------------------------------------------------------
+template <int D, int NT, bool KV8, int NWV>
+__global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const int32_t* __restrict__ seqlens, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
+    int bs, int T, int Hq, int Hkv, int Lmax, int gsize, int S, int chunk, int window,
+    float c_log2, uint16_t* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml) {
+    typedef DecodeShape<D> Sh;
+    typedef ExShape<D, KV8> Ex;
+    constexpr int KI = Sh::KI;
+    constexpr int EPL = Sh::EPL;
+    constexpr int HT = 16 * NT;
+
+    __shared__ float sm_o[HT * D];
+    __shared__ float sm_m[HT];
+    __shared__ float sm_l[HT];
+    __shared__ u32x4 k_tiles[NWV][32 * Sh::CPR];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int s = blockIdx.x % S;
+    const int bg = blockIdx.x / S;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int n = seqlens[b];
+    const int first = ex_first_key(n, T, window);
+    const int start = s * chunk;
+    const int end = min(start + chunk, n);
+    if (max(start, first) >= end) return;  // no token sees this split: the merge skips it
+
+    const int rs = Hkv * Ex::ROWB;  // bytes between consecutive rows of one KV head
+    const int R = T * gsize;        // query rows of the workgroup
+    const int h0 = g * gsize;
+    u32x4* kt = k_tiles[wave];
+    float cs = c_log2;
+    if constexpr (KV8) cs *= k_scale[g];
+
+    bf16x8 qB[NT][KI];
+    int lo[NT], hi[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + col;
+        const bool ok = r < R;
+        const int t = ok ? r / gsize : 0, hh = ok ? r % gsize : 0;
+        const uint16_t* qp = q + (((int64_t)b * T + t) * Hq + h0 + hh) * D + 8 * grp;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) qB[nt][i] = as_bf16x8(load16(qp + 32 * i, ok));
+        const int pos = n - T + t;
+        hi[nt] = ok ? pos : -1;
+        lo[nt] = window > 0 ? max(0, pos - window + 1) : 0;
+    }
+
+    f32x4 O[NT][EPL];
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+        l_run[nt] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) O[nt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // 32-aligned first step (start is a multiple of 32; the window start may not be)
+    const int kbeg = max(start, first & ~31);
+    const uint8_t* kseq = kc + (((int64_t)b * Lmax) * Hkv + g) * Ex::ROWB;
+    const uint8_t* vseq = vc + (((int64_t)b * Lmax) * Hkv + g) * Ex::ROWB;
+    // Issue the loads of the step starting at key0 (resources sized to its valid rows).
+    auto load = [&](int key0, ExStepData<D, KV8>& st) __attribute__((always_inline)) {
+        const uint8_t *kp, *vp;
+        if (block_table) {
+            const int64_t blk = block_table[(int64_t)b * max_blocks + key0 / bs];
+            const int64_t off = ((blk * bs + key0 % bs) * Hkv + g) * Ex::ROWB;
+            kp = kc + off;
+            vp = vc + off;
+        } else {
+            kp = kseq + (int64_t)key0 * rs;
+            vp = vseq + (int64_t)key0 * rs;
+        }
+        const int valid = min(end - key0, kDecodeStep);
+        const int nbytes = (valid - 1) * rs + Ex::ROWB;
+        ex_load_step<D, KV8>(st, make_rsrc(kp, nbytes), make_rsrc(vp, nbytes), rs, lane);
+    };
+    constexpr int stride = NWV * kDecodeStep;
+    if constexpr (KV8) {
+        // An E4M3 step moves half the bytes of a bf16 one: keep the next
+        // step's loads in flight while the current step is computed, so a
+        // wave has as many bytes outstanding as in the bf16 kernel.
+        ExStepData<D, KV8> cur;
+        int key0 = kbeg + wave * kDecodeStep;
+        if (key0 < end) load(key0, cur);
+        for (; key0 < end; key0 += stride) {
+            ExStepData<D, KV8> nxt;
+            if (key0 + stride < end) load(key0 + stride, nxt);
+            ex_stage_k<D, KV8>(cur, kt, lane);
+            ex_compute_step<D, NT, KV8>(cur, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
+            cur = nxt;
+        }
+    } else {
+        for (int key0 = kbeg + wave * kDecodeStep; key0 < end; key0 += stride) {
+            ExStepData<D, KV8> st;
+            load(key0, st);
+            ex_stage_k<D, KV8>(st, kt, lane);
+            ex_compute_step<D, NT, KV8>(st, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
+        }
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        l_run[nt] += __shfl_xor(l_run[nt], 16);
+        l_run[nt] += __shfl_xor(l_run[nt], 32);
+    }
+    // Combine the waves of the workgroup in LDS, one wave at a time.
+    if (wave == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 16 * nt + 4 * grp + r;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_o[h * D + EPL * col + e] = O[nt][e][r];
+            }
+            if (grp == 0) {
+                sm_m[16 * nt + col] = m_run[nt];
+                sm_l[16 * nt + col] = l_run[nt];
+            }
+        }
+    }
+    for (int w = 1; w < NWV; ++w) {
+        __syncthreads();
+        if (wave == w) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int h = 16 * nt + 4 * grp + r;
+                    const float mo = sm_m[h];
+                    const float mw = __shfl(m_run[nt], 4 * grp + r);
+                    const float M = fmaxf(mo, mw);
+                    const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
+                    const float fb = M == kNegInf ? 0.f : fast_exp2(mw - M);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const int idx = h * D + EPL * col + e;
+                        sm_o[idx] = fa * sm_o[idx] + fb * O[nt][e][r];
+                    }
+                }
+                const float mo = sm_m[16 * nt + col];
+                const float lw = sm_l[16 * nt + col];
+                const float M = fmaxf(mo, m_run[nt]);
+                const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
+                const float fb = M == kNegInf ? 0.f : fast_exp2(m_run[nt] - M);
+                if (grp == 0) {
+                    sm_m[16 * nt + col] = M;
+                    sm_l[16 * nt + col] = fa * lw + fb * l_run[nt];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const float vsc = KV8 ? v_scale[g] : 1.f;
+    constexpr int C8 = D / 8;
+    const int items = R * C8;
+    for (int it = threadIdx.x; it < items; it += 64 * NWV) {
+        const int h = it / C8;
+        const int c = (it % C8) * 8;
+        const int t = h / gsize, hh = h % gsize;
+        const float* src = sm_o + h * D + c;
+        const int64_t row = ((int64_t)b * T + t) * Hq + h0 + hh;
+        if (S == 1) {
+            const float l = sm_l[h];
+            const float f = l > 0.f ? vsc / l : 0.f;
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2_rne(src[2 * j] * f, src[2 * j + 1] * f);
+            *reinterpret_cast<u32x4*>(out + row * D + c) = o;
+        } else {
+            float* dst = ws_acc + (row * S + s) * D + c;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{src[0] * vsc, src[1] * vsc, src[2] * vsc, src[3] * vsc};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4] * vsc, src[5] * vsc, src[6] * vsc, src[7] * vsc};
+            if (c == 0) {
+                ws_ml[(row * S + s) * 2] = sm_m[h];
+                ws_ml[(row * S + s) * 2 + 1] = sm_l[h];
+            }
+        }
+    }
+}
+
+// Merge of the split partials of one (b, t, h) row over the splits some
+// token of sequence b can see: s in [first / chunk, ceil(n / chunk)).
+template <int D>
+__global__ __launch_bounds__(64) void decode_ex_merge(const float* __restrict__ ws_acc,
+                                                      const float* __restrict__ ws_ml,
+                                                      const int32_t* __restrict__ seqlens, int T,
+                                                      int Hq, int S, int chunk, int window,
+                                                      uint16_t* __restrict__ out) {
+    constexpr int PER = D / 64;
+    const int64_t row = blockIdx.x;
+    const int b = (int)(row / ((int64_t)T * Hq));
+    const int n = seqlens[b];
+    const int s0 = ex_first_key(n, T, window) / chunk;
+    const int se = min(S, (n + chunk - 1) / chunk);
+    const int c0 = threadIdx.x * PER;
+    const float* ml = ws_ml + row * S * 2;
+    float M = kNegInf;
+    for (int s = s0; s < se; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f, acc[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+    for (int s = s0; s < se; ++s) {
+        const float f = ml[2 * s] == kNegInf ? 0.f : fast_exp2(ml[2 * s] - M);
+        L += f * ml[2 * s + 1];
+        const float* a = ws_acc + (row * S + s) * D + c0;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] += f * a[p];
+    }
+    uint16_t* dst = out + row * D + c0;
+    if (PER == 2)
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2_rne(L > 0.f ? acc[0] / L : 0.f, L > 0.f ? acc[PER - 1] / L : 0.f);
+    else
+        dst[0] = (uint16_t)f32_to_bf16_rne(L > 0.f ? acc[0] / L : 0.f);
+}
+
+// Append: row t of k_new/v_new [B,T,Hkv,d] (ROWB bytes per KV head) goes to
+// cache row seqlens[b] - T + t, contiguous or paged.  One workgroup per
+// (b, t, g); lanes copy 16-byte pieces.
+template <int ROWB>
+__global__ __launch_bounds__(64) void append_rows(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                  const uint8_t* __restrict__ k_new,
+                                                  const uint8_t* __restrict__ v_new,
+                                                  const int32_t* __restrict__ seqlens,
+                                                  const int32_t* __restrict__ block_table,
+                                                  int max_blocks, int bs, int T, int Hkv, int Lmax) {
+    constexpr int PIECES = ROWB / 16;
+    const int g = blockIdx.x % Hkv;
+    const int bt = blockIdx.x / Hkv;
+    const int b = bt / T, t = bt % T;
+    const int j = seqlens[b] - T + t;
+    int64_t dst;
+    if (block_table) {
+        const int64_t blk = block_table[(int64_t)b * max_blocks + j / bs];
+        dst = ((blk * bs + j % bs) * Hkv + g) * ROWB;
+    } else {
+        dst = (((int64_t)b * Lmax + j) * Hkv + g) * ROWB;
+    }
+    const int64_t src = ((int64_t)bt * Hkv + g) * ROWB;
+    for (int p = threadIdx.x; p < PIECES; p += 64) {
+        *reinterpret_cast<u32x4*>(kc + dst + 16 * p) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * p);
+        *reinterpret_cast<u32x4*>(vc + dst + 16 * p) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * p);
+    }
+}
+
+}  // namespace gqa

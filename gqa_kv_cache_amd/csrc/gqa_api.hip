@@ -12,6 +12,7 @@
 #include "gqa.h"
 #include "common.hpp"
 #include "decode.hpp"
+#include "decode_ex.hpp"
 #include "prefill.hpp"
 
 namespace {
@@ -109,6 +110,88 @@ void launch_split_bf16(int nt, dim3 grid, hipStream_t st, const uint16_t* q, con
         case 3: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 3>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
         default: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 4>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
     }
+}
+
+// ----- extended decode ------------------------------------------------------
+
+struct ExPlan {
+    int splits, chunk, elt;
+    size_t ws_bytes;
+};
+
+gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan* plan) {
+    if (a->B <= 0 || a->T <= 0 || a->Lmax <= 0 || a->window < 0) return GQA_ERR_SHAPE;
+    gqa_status st = check_heads(a->Hq, a->Hkv, a->d);
+    if (st != GQA_OK) return st;
+    if (a->dtype != GQA_BF16) return GQA_ERR_DTYPE;
+    if (a->kv_dtype != GQA_BF16 && a->kv_dtype != GQA_FP8_E4M3) return GQA_ERR_DTYPE;
+    if ((int64_t)a->T * (a->Hq / a->Hkv) > kMaxGroup) return GQA_ERR_UNSUPPORTED;
+    if (a->block_table) {
+        if (a->block_size < 32 || a->block_size % 32 != 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
+            return GQA_ERR_SHAPE;
+        if ((int64_t)a->max_blocks * a->block_size != a->Lmax) return GQA_ERR_SHAPE;
+    }
+    if (a->num_splits < 0 || a->num_splits > a->Lmax) return GQA_ERR_UNSUPPORTED;
+    int64_t chunk;
+    if (a->num_splits == 0) {
+        int cus = 0;
+        if (query_device) {
+            st = current_cu_count(&cus);
+            if (st != GQA_OK) return st;
+        } else {
+            cus = 256;
+        }
+        const int64_t pairs = (int64_t)a->B * a->Hkv;
+        int64_t splits = cdiv(cus, pairs);
+        if (splits < cdiv(a->Lmax, kMaxChunk)) splits = cdiv(a->Lmax, kMaxChunk);
+        chunk = cdiv(a->Lmax, splits);
+    } else {
+        chunk = cdiv(a->Lmax, a->num_splits);
+    }
+    // pieces start on 32-key steps, so a step never crosses a cache block
+    chunk = cdiv(chunk, gqa::kDecodeStep) * gqa::kDecodeStep;
+    const int64_t splits = cdiv(a->Lmax, chunk);
+    const int64_t rows = (int64_t)a->B * a->T * a->Hq;
+    if ((int64_t)a->B * a->Hkv * splits > INT_MAX || rows > INT_MAX) return GQA_ERR_SHAPE;
+    plan->splits = (int)splits;
+    plan->chunk = (int)chunk;
+    plan->elt = a->kv_dtype == GQA_FP8_E4M3 ? 1 : 2;
+    plan->ws_bytes = splits > 1 ? (size_t)rows * splits * (a->d + 2) * sizeof(float) : 0;
+    return GQA_OK;
+}
+
+// Waves per workgroup of the extended kernel: an E4M3 step moves half the
+// bytes of a bf16 step, so twice the waves keep as many bytes in flight
+// (up to 32 query rows; more rows need more registers than 8 waves allow).
+template <bool KV8, int NT> constexpr int ex_waves() { return KV8 && NT <= 2 ? 8 : 4; }
+
+template <int D, bool KV8>
+void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_args* a, const ExPlan& p,
+                      float c, float* wa, float* wm) {
+    dim3 block;
+    auto q = static_cast<const uint16_t*>(a->q);
+    auto k = static_cast<const uint8_t*>(a->k_cache);
+    auto v = static_cast<const uint8_t*>(a->v_cache);
+    auto o = static_cast<uint16_t*>(a->out);
+    const int gs = a->Hq / a->Hkv;
+#define GQA_EX_ARGS q, k, v, a->seqlens, a->k_scale, a->v_scale, a->block_table, a->max_blocks, \
+                    a->block_size, a->T, a->Hq, a->Hkv, a->Lmax, gs, p.splits, p.chunk, a->window, c, o, wa, wm
+    switch (nt) {
+        case 1: block = dim3(64 * ex_waves<KV8, 1>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 1, KV8, ex_waves<KV8, 1>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 2: block = dim3(64 * ex_waves<KV8, 2>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 2, KV8, ex_waves<KV8, 2>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 3: block = dim3(64 * ex_waves<KV8, 3>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 3, KV8, ex_waves<KV8, 3>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        default: block = dim3(64 * ex_waves<KV8, 4>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 4, KV8, ex_waves<KV8, 4>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+    }
+#undef GQA_EX_ARGS
+}
+
+template <int ROWB>
+void launch_append(hipStream_t hs, const gqa_decode_ex_args* a) {
+    dim3 grid((unsigned)((int64_t)a->B * a->T * a->Hkv));
+    hipLaunchKernelGGL((gqa::append_rows<ROWB>), grid, dim3(64), 0, hs,
+                       static_cast<uint8_t*>(a->k_cache), static_cast<uint8_t*>(a->v_cache),
+                       static_cast<const uint8_t*>(a->k_new), static_cast<const uint8_t*>(a->v_new),
+                       a->seqlens, a->block_table, a->max_blocks, a->block_size, a->T, a->Hkv, a->Lmax);
 }
 
 }  // namespace
@@ -218,6 +301,69 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
             else
                 hipLaunchKernelGGL((gqa::decode_merge<64, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
         }
+        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    }
+    return GQA_OK;
+}
+
+gqa_status gqa_decode_ex_workspace_size(const gqa_decode_ex_args* a, size_t* bytes) {
+    if (!a || !bytes) return GQA_ERR_NULL;
+    ExPlan plan;
+    gqa_status st = plan_decode_ex(a, true, &plan);
+    if (st != GQA_OK) return st;
+    *bytes = plan.ws_bytes;
+    return GQA_OK;
+}
+
+gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
+    if (!a) return GQA_ERR_NULL;
+    if (!a->q || !a->k_cache || !a->v_cache || !a->seqlens || !a->out) return GQA_ERR_NULL;
+    if ((a->k_new == nullptr) != (a->v_new == nullptr)) return GQA_ERR_NULL;
+    if (a->kv_dtype == GQA_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return GQA_ERR_NULL;
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->out))
+        return GQA_ERR_ALIGN;
+    if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return GQA_ERR_ALIGN;
+    // validate everything before the first device query
+    ExPlan plan;
+    gqa_status st = plan_decode_ex(a, false, &plan);
+    if (st != GQA_OK) return st;
+    st = plan_decode_ex(a, true, &plan);
+    if (st != GQA_OK) return st;
+    if (plan.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < plan.ws_bytes || !aligned16(a->workspace)))
+        return GQA_ERR_WORKSPACE;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int S = plan.splits;
+    const int64_t rows = (int64_t)a->B * a->T * a->Hq;
+    float* ws_acc = plan.ws_bytes ? static_cast<float*>(a->workspace) : nullptr;
+    float* ws_ml = plan.ws_bytes ? ws_acc + rows * S * a->d : nullptr;
+    const bool fp8 = a->kv_dtype == GQA_FP8_E4M3;
+    (void)hipGetLastError();
+    if (a->k_new) {
+        const int rowb = a->d * plan.elt;
+        if (rowb == 256) launch_append<256>(hs, a);
+        else if (rowb == 128) launch_append<128>(hs, a);
+        else launch_append<64>(hs, a);
+        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    }
+    const int nt = (a->T * (a->Hq / a->Hkv) + 15) / 16;
+    const float c = a->scale * gqa::kLog2e;
+    dim3 grid((unsigned)((int64_t)a->B * a->Hkv * S));
+    if (a->d == 128) {
+        if (fp8) launch_decode_ex<128, true>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else launch_decode_ex<128, false>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+    } else {
+        if (fp8) launch_decode_ex<64, true>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else launch_decode_ex<64, false>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+    }
+    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+    if (S > 1) {
+        dim3 mgrid((unsigned)rows);
+        auto o = static_cast<uint16_t*>(a->out);
+        if (a->d == 128)
+            hipLaunchKernelGGL((gqa::decode_ex_merge<128>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, S, plan.chunk, a->window, o);
+        else
+            hipLaunchKernelGGL((gqa::decode_ex_merge<64>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, S, plan.chunk, a->window, o);
         if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     }
     return GQA_OK;

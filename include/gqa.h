@@ -39,7 +39,11 @@
 extern "C" {
 #endif
 
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+typedef enum {
+    GQA_F32 = 0,
+    GQA_BF16 = 1,
+    GQA_FP8_E4M3 = 2 /* OCP 8-bit float E4M3 (bias 7, no infinities); KV caches of gqa_decode_ex only */
+} gqa_dtype;
 
 typedef enum {
     GQA_OK = 0,
@@ -128,6 +132,81 @@ gqa_status gqa_decode_workspace_size(int B, int Hq, int Hkv, int d, int Lmax, gq
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P, int Hq,
                        int Hkv, int d, int causal, float scale, gqa_dtype dtype, void *out,
                        void *stream);
+
+/* ------------------------------------------------------------------------
+ * Extended decode: several new tokens, append, FP8 cache, paged cache,
+ * sliding window.
+ *
+ * The decode step of "GQA reading notes", Algorithm 2, with the cache update
+ * (the new K/V rows are appended before attending) done by the same call,
+ * and generalised in four ways the pages combine with GQA: several new query
+ * tokens per sequence verified at once against one read of the cache, a
+ * cache stored in FP8, a cache managed in fixed-size blocks addressed through
+ * a block table, and attention restricted to the most recent keys ("GQA
+ * reading notes", sections "关联工作：GQA 之后又发生了什么" and the engineering
+ * notes of "复现性"; "从MHA到GQA", section on what each attention-efficiency
+ * technique changes).
+ *
+ * For sequence b with n = seqlens[b] valid rows (the T new ones included),
+ * new token t sits at position pos = n - T + t and, for every query head h
+ * (KV head g = h / (Hq/Hkv)),
+ *   out[b,t,h,:] = sum_j softmax_j(scale * <q[b,t,h,:], K[b,j,g,:]>) V[b,j,g,:]
+ * over keys j in [lo, pos], lo = max(0, pos - window + 1) if window > 0,
+ * else 0: causal among the new tokens, as in prefill.
+ *
+ * Fields of gqa_decode_ex_args (all pointers are DEVICE memory, 16-byte
+ * aligned where they hold rows):
+ *   q        [B, T, Hq, d] bf16 (dtype must be GQA_BF16)
+ *   out      [B, T, Hq, d] bf16
+ *   k_cache, v_cache   the cache, element type kv_dtype (GQA_BF16 or
+ *            GQA_FP8_E4M3): contiguous [B, Lmax, Hkv, d] when block_table is
+ *            NULL; otherwise a pool [num_blocks, block_size, Hkv, d] and row j
+ *            of sequence b is row j % block_size of block
+ *            block_table[b * max_blocks + j / block_size].  Written when
+ *            k_new is given; read otherwise.
+ *   seqlens  [B] int32: valid rows per sequence AFTER the append.
+ *            Precondition (not checked, device data): T <= seqlens[b] <= Lmax.
+ *   block_table  [B, max_blocks] int32 or NULL.  block_size must be a multiple
+ *            of 32; Lmax must equal max_blocks * block_size.  Precondition:
+ *            every entry used is in [0, num_blocks).
+ *   k_scale, v_scale  [Hkv] fp32, GQA_FP8_E4M3 only: K row values are
+ *            e4m3(byte) * k_scale[g], V likewise with v_scale[g].
+ *   k_new, v_new  [B, T, Hkv, d] in kv_dtype, or both NULL.  When given they
+ *            are first stored, byte for byte, at rows seqlens[b] - T + t.
+ *   window   0 = every key; W > 0 = the last W keys of each token.
+ *   T * (Hq/Hkv) <= 64; d 64 or 128; B, T, Hq, Hkv, Lmax >= 1.
+ *   num_splits, workspace, workspace_bytes  as for gqa_decode; the size comes
+ *            from gqa_decode_ex_workspace_size.
+ *
+ * Returns GQA_OK or an error code (conventions at the top of this file).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const void *q;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *seqlens;
+    int B, T, Hq, Hkv, d, Lmax;
+    float scale;
+    gqa_dtype dtype;
+    gqa_dtype kv_dtype;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *block_table;
+    int block_size, max_blocks, num_blocks;
+    int window;
+    const void *k_new;
+    const void *v_new;
+    void *out;
+    void *workspace;
+    size_t workspace_bytes;
+    int num_splits;
+} gqa_decode_ex_args;
+
+gqa_status gqa_decode_ex(const gqa_decode_ex_args *args, void *stream);
+
+/* Workspace bytes gqa_decode_ex needs for these arguments (0 when none).
+ * Only the shape, dtype, paging and num_splits fields are read. */
+gqa_status gqa_decode_ex_workspace_size(const gqa_decode_ex_args *args, size_t *bytes);
 
 /* ------------------------------------------------------------------------
  * Counts (host only, exact integers).

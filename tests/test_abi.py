@@ -152,3 +152,79 @@ def test_prefill_counts_match_oracle(B, P, Hq, Hkv, d, causal):
 
 def test_prefill_flops_headline_value():
     assert gqa.prefill_flops(2, 4096, 32, 128, True) == 274945015808
+
+
+# --- gqa_decode_ex ---------------------------------------------------------
+
+from gqa_kv_cache_amd._native import DecodeExArgs  # noqa: E402
+
+
+def _ex_args(**kw):
+    a = DecodeExArgs()
+    base = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, seqlens=FAKE, B=2, T=2, Hq=8, Hkv=2, d=128,
+                Lmax=64, scale=0.1, dtype=gqa.BF16, kv_dtype=gqa.BF16, k_scale=None, v_scale=None,
+                block_table=None, block_size=0, max_blocks=0, num_blocks=0, window=0, k_new=None,
+                v_new=None, out=FAKE, workspace=None, workspace_bytes=0, num_splits=1)
+    base.update(kw)
+    for name, val in base.items():
+        setattr(a, name, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), Status.ERR_NULL),
+    (dict(out=None), Status.ERR_NULL),
+    (dict(seqlens=None), Status.ERR_NULL),
+    (dict(k_new=FAKE), Status.ERR_NULL),                         # v_new missing
+    (dict(kv_dtype=gqa.FP8_E4M3), Status.ERR_NULL),              # scales missing
+    (dict(q=FAKE + 2), Status.ERR_ALIGN),
+    (dict(k_new=FAKE + 8, v_new=FAKE), Status.ERR_ALIGN),
+    (dict(T=0), Status.ERR_SHAPE),
+    (dict(window=-1), Status.ERR_SHAPE),
+    (dict(B=0), Status.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), Status.ERR_GROUP),
+    (dict(d=32), Status.ERR_HEADDIM),
+    (dict(dtype=gqa.F32), Status.ERR_DTYPE),
+    (dict(kv_dtype=gqa.F32), Status.ERR_DTYPE),
+    (dict(T=17, Hq=8, Hkv=2), Status.ERR_UNSUPPORTED),           # 17 tokens x group of 4 > 64 rows
+    (dict(block_table=FAKE, block_size=16, max_blocks=4, num_blocks=8), Status.ERR_SHAPE),
+    (dict(block_table=FAKE, block_size=32, max_blocks=3, num_blocks=8), Status.ERR_SHAPE),  # Lmax != 96
+    (dict(block_table=FAKE, block_size=32, max_blocks=2, num_blocks=0), Status.ERR_SHAPE),
+    (dict(num_splits=65), Status.ERR_UNSUPPORTED),
+    (dict(num_splits=2), Status.ERR_WORKSPACE),
+    (dict(num_splits=2, workspace=FAKE, workspace_bytes=64), Status.ERR_WORKSPACE),
+])
+def test_decode_ex_validation(kw, expect):
+    a = _ex_args(**kw)
+    assert gqa.load().gqa_decode_ex(ctypes.byref(a), None) == expect
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d,Lmax,ns", [(2, 2, 8, 2, 128, 64, 1), (2, 2, 8, 2, 128, 64, 2),
+                                                  (3, 4, 32, 8, 64, 1000, 7), (1, 1, 4, 4, 128, 33, 33)])
+def test_decode_ex_workspace_size(B, T, Hq, Hkv, d, Lmax, ns):
+    a = _ex_args(B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, Lmax=Lmax, num_splits=ns)
+    got = ctypes.c_size_t(0)
+    assert gqa.load().gqa_decode_ex_workspace_size(ctypes.byref(a), ctypes.byref(got)) == 0
+    # pieces of ceil(Lmax / ns) keys rounded up to whole 32-key steps
+    chunk = -(-Lmax // ns)
+    chunk = -(-chunk // 32) * 32
+    splits = -(-Lmax // chunk)
+    want = 0 if splits == 1 else B * T * Hq * splits * (d + 2) * 4
+    assert got.value == want
+
+
+def test_decode_ex_struct_layout_matches_header(tmp_path):
+    fields = [f[0] for f in DecodeExArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join('printf("%%s %%zu\\n", "%s", offsetof(gqa_decode_ex_args, %s));\n' % (f, f)
+                   for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gqa.h"\nint main(void){\n'
+                   'printf("sizeof %zu\\n", sizeof(gqa_decode_ex_args));\n' + body + "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                         check=True).stdout.splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(DecodeExArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(DecodeExArgs, f).offset, f

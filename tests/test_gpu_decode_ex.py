@@ -1,0 +1,167 @@
+"""GPU parity of gqa_decode_ex against the fp64 CPU oracle (needs an MI355X).
+
+Covers several new tokens per sequence, the append of their K/V rows, FP8
+(E4M3) caches with per-KV-head scales, paged caches and sliding windows, alone
+and combined, with forced and automatic splits.  Tolerance (bf16 q and out,
+fp32 accumulation): |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise.
+Cache rows past each length, pool blocks no sequence uses and the rows of the
+new tokens before the append hold NaN, so a stray read would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import gqa_kv_cache_amd as gqa
+from oracle import reference as orc
+from tests.gpu_util import from_dev, to_dev
+from tests.helpers import bf16_tol_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_cache(a):
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return to_dev(a)
+
+
+def run_ex(c, append=True, num_splits=0):
+    """Run gqa_decode_ex on case c; returns (out, k_cache, v_cache) on the device."""
+    q = to_dev(c.q)
+    k = _dev_cache(c.k_pre if append else c.k)
+    v = _dev_cache(c.v_pre if append else c.v)
+    sl = torch.from_numpy(c.seqlens).cuda()
+    kw = {}
+    if c.kv == "fp8":
+        kw["k_scale"] = torch.from_numpy(c.k_scale).cuda()
+        kw["v_scale"] = torch.from_numpy(c.v_scale).cuda()
+    if c.block_table is not None:
+        kw["block_table"] = torch.from_numpy(c.block_table).cuda()
+        kw["block_size"] = c.block_size
+    if append:
+        kw["k_new"] = _dev_cache(c.k_new)
+        kw["v_new"] = _dev_cache(c.v_new)
+    out = gqa.decode_ex(q, k, v, sl, scale=c.scale, window=c.window, num_splits=num_splits, **kw)
+    torch.cuda.synchronize()
+    return out, k, v
+
+
+def oracle_ex(c, rows=None):
+    return orc.decode_ex(c.q, c.k, c.v, c.seqlens, c.scale, k_scale=c.k_scale, v_scale=c.v_scale,
+                         block_table=c.block_table, block_size=c.block_size, window=c.window,
+                         rows=rows)
+
+
+def check(c, got, ref):
+    ok, err = bf16_tol_ok(got, ref)
+    assert ok, "%s: max abs err %.3g" % (c.name, err)
+    assert np.all(np.isfinite(got))
+    return err
+
+
+def case(B=3, T=2, Hq=16, Hkv=4, d=128, Lmax=256, seqlens=(256, 97, 5), kv="same", paged=False,
+         block_size=64, window=0, seed=40):
+    name = "ex_B%d_T%d_Hq%d_Hkv%d_d%d_L%d_%s%s_w%d" % (B, T, Hq, Hkv, d, Lmax, kv,
+                                                    "_paged%d" % block_size if paged else "", window)
+    return gi.decode_ex_case(B, T, Hq, Hkv, d, Lmax, list(seqlens), "bf16", seed=seed, kv=kv,
+                             paged=paged, block_size=block_size, window=window, name=name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T,Hq,Hkv", [(1, 8, 8), (1, 32, 4), (2, 16, 4), (4, 32, 4), (8, 64, 8),
+                                      (3, 24, 2), (16, 8, 2), (64, 4, 4)])
+def test_tokens_and_groups(d, T, Hq, Hkv):
+    c = case(T=T, Hq=Hq, Hkv=Hkv, d=d, seqlens=(256, 97, max(T, 5)), seed=41)
+    out, _, _ = run_ex(c)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
+def test_splits(kv, splits):
+    c = case(kv=kv, T=3, seqlens=(256, 200, 33), seed=42)
+    out, _, _ = run_ex(c, num_splits=splits)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 4])
+def test_fp8_cache(d, T):
+    c = case(kv="fp8", d=d, T=T, seed=43)
+    out, _, _ = run_ex(c)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("block_size", [32, 64, 128])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_paged(kv, block_size, splits):
+    c = case(kv=kv, paged=True, block_size=block_size, T=2, seed=44)
+    out, _, _ = run_ex(c, num_splits=splits)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+@pytest.mark.parametrize("window", [1, 5, 31, 32, 33, 100, 255, 4096])
+@pytest.mark.parametrize("splits", [0, 4])
+def test_window(window, splits):
+    c = case(window=window, T=3, seqlens=(256, 130, 7), seed=45)
+    out, _, _ = run_ex(c, num_splits=splits)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+def test_everything_together():
+    c = case(B=4, T=4, Hq=32, Hkv=4, kv="fp8", paged=True, block_size=32, window=45,
+             seqlens=(256, 161, 64, 4), seed=46)
+    for splits in (0, 1, 5):
+        out, _, _ = run_ex(c, num_splits=splits)
+        check(c, from_dev(out), oracle_ex(c))
+
+
+@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", False), ("fp8", True)])
+def test_append_writes_cache_rows_exactly(kv, paged):
+    c = case(kv=kv, paged=paged, T=4, seed=47)
+    out, k, v = run_ex(c, append=True)
+    want_k, want_v = c.k_pre.copy(), c.v_pre.copy()
+    orc.append(want_k, want_v, c.k_new, c.v_new, c.seqlens, block_table=c.block_table,
+               block_size=c.block_size)
+    got_k = k.view(torch.uint8).cpu().numpy().reshape(-1)
+    got_v = v.view(torch.uint8).cpu().numpy().reshape(-1)
+    assert np.array_equal(got_k, want_k.view(np.uint8).reshape(-1))
+    assert np.array_equal(got_v, want_v.view(np.uint8).reshape(-1))
+    check(c, from_dev(out), oracle_ex(c))
+
+
+def test_without_append_reads_the_cache():
+    c = case(T=2, seed=48)
+    out, _, _ = run_ex(c, append=False)
+    check(c, from_dev(out), oracle_ex(c))
+
+
+def test_single_token_matches_plain_decode():
+    c = case(T=1, Hq=64, Hkv=8, seqlens=(256, 255, 1), seed=49)
+    out, k, v = run_ex(c, append=False)
+    plain = gqa.decode(to_dev(np.ascontiguousarray(c.q[:, 0])), k, v,
+                       torch.from_numpy(c.seqlens).cuda(), c.scale)
+    torch.cuda.synchronize()
+    ok, err = bf16_tol_ok(from_dev(out)[:, 0], from_dev(plain))
+    assert ok, err
+
+
+def test_fp8_70b_layer_sampled():
+    """The 70B-class layer shape with an FP8 cache and 4 new tokens per sequence,
+    sampled rows against the oracle."""
+    c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096] * 32, "bf16", seed=50, kv="fp8",
+                          invalid="zero", name="ex_fp8_B32_T4_Hq64_Hkv8_d128_L4096")
+    out, _, _ = run_ex(c)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))
+    got = from_dev(out).reshape(-1, 128)[rows]
+    check(c, got, oracle_ex(c, rows=rows))
+
+
+def test_run_twice_bitwise():
+    c = case(kv="fp8", paged=True, T=3, window=50, seed=51)
+    a, _, _ = run_ex(c, num_splits=3)
+    b, _, _ = run_ex(c, num_splits=3)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
