@@ -45,6 +45,7 @@ EXPORTS = (
     "gqa_status_str", "gqa_decode", "gqa_decode_num_splits", "gqa_decode_workspace_size",
     "gqa_prefill", "gqa_kv_cache_elems", "gqa_decode_bytes", "gqa_decode_flops",
     "gqa_prefill_flops", "gqa_prefill_bytes", "gqa_decode_ex", "gqa_decode_ex_workspace_size",
+    "gqa_prefill_ex",
 )
 
 
@@ -85,6 +86,8 @@ def load():
     lib.gqa_decode_workspace_size.restype = ci
     lib.gqa_prefill.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
     lib.gqa_prefill.restype = ci
+    lib.gqa_prefill_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, vp]
+    lib.gqa_prefill_ex.restype = ci
     lib.gqa_kv_cache_elems.argtypes = [u64, u64, u64]
     lib.gqa_kv_cache_elems.restype = u64
     lib.gqa_decode_bytes.argtypes = [vp, ci, ci, ci, ci, ci]
@@ -284,8 +287,11 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
     return out
 
 
-def prefill(q, k, v, causal=True, scale=None, out=None):
-    """GQA prefill.  q [B,P,Hq,d]; k, v [B,P,Hkv,d]; bfloat16.  Returns ``out``."""
+def prefill(q, k, v, causal=True, scale=None, out=None, window=0):
+    """GQA prefill.  q [B,P,Hq,d]; k, v [B,P,Hkv,d]; bfloat16.  Returns ``out``.
+
+    ``window`` > 0 (causal only): position i attends to the last ``window``
+    positions up to and including i (gqa_prefill_ex)."""
     import torch
     lib = load()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -309,9 +315,10 @@ def prefill(q, k, v, causal=True, scale=None, out=None):
             raise ValueError("gqa: out must match q in shape and dtype")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, P, Hq, Hkv, d,
-                             1 if causal else 0, float(scale), dt, out.data_ptr(), stream)
-    _check(st, "gqa_prefill")
+        st = lib.gqa_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, P, Hq, Hkv, d,
+                                1 if causal else 0, int(window), float(scale), dt, out.data_ptr(),
+                                stream)
+    _check(st, "gqa_prefill_ex")
     return out
 
 

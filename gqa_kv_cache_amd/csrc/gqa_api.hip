@@ -369,25 +369,32 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
     return GQA_OK;
 }
 
-gqa_status gqa_prefill(const void* q, const void* k, const void* v, int B, int P, int Hq, int Hkv,
-                       int d, int causal, float scale, gqa_dtype dtype, void* out, void* stream) {
+gqa_status gqa_prefill_ex(const void* q, const void* k, const void* v, int B, int P, int Hq,
+                          int Hkv, int d, int causal, int window, float scale, gqa_dtype dtype,
+                          void* out, void* stream) {
     if (!q || !k || !v || !out) return GQA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
-    if (B <= 0 || P <= 0) return GQA_ERR_SHAPE;
+    if (B <= 0 || P <= 0 || window < 0) return GQA_ERR_SHAPE;
     gqa_status st = check_heads(Hq, Hkv, d);
     if (st != GQA_OK) return st;
     if (dtype != GQA_BF16) return GQA_ERR_DTYPE;
+    if (window > 0 && !causal) return GQA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * cdiv(P, gqa::kPrefillRows) > INT_MAX) return GQA_ERR_SHAPE;
     // byte offsets inside one sequence's K/V are 32-bit
     if ((int64_t)(P + gqa::kPrefillBN) * Hkv * d * 2 > INT_MAX) return GQA_ERR_SHAPE;
     (void)hipGetLastError();
     if (!gqa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                             static_cast<const uint16_t*>(v), B, P, Hq, Hkv, d, causal != 0,
+                             static_cast<const uint16_t*>(v), B, P, Hq, Hkv, d, causal != 0, window,
                              scale * gqa::kLog2e, static_cast<uint16_t*>(out),
                              static_cast<hipStream_t>(stream)))
         return GQA_ERR_HIP;
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     return GQA_OK;
+}
+
+gqa_status gqa_prefill(const void* q, const void* k, const void* v, int B, int P, int Hq, int Hkv,
+                       int d, int causal, float scale, gqa_dtype dtype, void* out, void* stream) {
+    return gqa_prefill_ex(q, k, v, B, P, Hq, Hkv, d, causal, 0, scale, dtype, out, stream);
 }
 
 uint64_t gqa_kv_cache_elems(uint64_t L, uint64_t Hkv, uint64_t d) { return 2ull * L * Hkv * d; }

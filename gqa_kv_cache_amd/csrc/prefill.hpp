@@ -39,6 +39,11 @@ constexpr int kPrefillBN = 64;                     // keys per LDS tile
 constexpr int kPrefillMT = 2;                      // 16-row query tiles per wave
 constexpr int kPrefillRows = 16 * kPrefillMT * 2;  // fewest query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;              // log2 of the largest weight allowed
+// Reference of a row that has seen no visible key: the lowest finite float.
+// Masked (-inf) scores against it give weight 2^-inf = 0 (never NaN), any
+// finite score raises it before weights are formed, and a rescale against it
+// gives factor 0 (or 1 while the row still has seen nothing).
+constexpr float kNoScoreYet = -3.4028234663852886e38f;
 
 template <int D, int NW, int BN> struct PrefillShape {
     static constexpr int KI = D / 32;          // 32-wide head-dim slices of the score MFMA
@@ -74,7 +79,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D, int MT, int NW, int BN>
 __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, float c_log2,
+    int P, int Hq, int Hkv, int gsize, int hw, int nbgh, int nrb, int causal, int window, float c_log2,
     uint16_t* __restrict__ out) {
     typedef PrefillShape<D, NW, BN> Sh;
     constexpr int KI = Sh::KI;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     float m_ref[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        m_ref[mt] = kNegInf;
+        m_ref[mt] = kNoScoreYet;
         osum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < NB; ++e) O[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = kc0 + 8 * grp + 4 * t + r;
-                    if (key >= P || (causal && key > qrow)) sc[mt][t][r] = kNegInf;
+                    if (key >= P || (causal && key > qrow) || (window > 0 && key <= qrow - window))
+                        sc[mt][t][r] = kNegInf;
                 }
         }
     };
@@ -305,6 +311,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const int kv_end = causal ? min(P, i0 + rows_wg) : P;
     const int wave_last_row = min(iw + WR, P) - 1;
     const int ntiles = (kv_end + BN - 1) / BN;
+    // sliding window (causal only): row i sees keys [i - window + 1, i]; the
+    // workgroup starts at the first tile its first row can see
+    const int jt_lo = window > 0 ? max(0, i0 - window + 1) / BN : 0;
     // keys this wave needs: up to kv_end, and up to its last row when causal
     const int lim = causal ? min(kv_end, wave_last_row + 1) : kv_end;
 
@@ -317,7 +326,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         typedef std::integral_constant<int, 1 - decltype(stage)::value> Other;
         const int j0 = jt * BN;
         if (jt + 1 < ntiles) fill(Other{}, j0 + BN);
-        const bool full = j0 + BN <= lim && j0 + BN <= P && (!causal || j0 + BN - 1 <= iw);
+        const bool full = j0 + BN <= lim && j0 + BN <= P && (!causal || j0 + BN - 1 <= iw) &&
+                          (window <= 0 || j0 > wave_last_row - window);
         if (full) {
 #pragma unroll 1
             for (int c = 0; c < CPT; ++c) {
@@ -334,6 +344,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
             for (int c = 0; c < CPT; ++c) {
                 const int kc0 = j0 + 32 * c;
                 if (kc0 >= lim) break;
+                if (window > 0 && kc0 + 31 <= iw - window) continue;  // below every row's window
                 f32x4 sc[MT][2];
                 scores(stage, c, sc);
                 mask(kc0, sc);
@@ -347,10 +358,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         __syncthreads();
     };
 
-    fill(Stage0{}, 0);
+    fill(Stage0{}, jt_lo * BN);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int jt = 0; jt < ntiles; jt += 2) {
+    for (int jt = jt_lo; jt < ntiles; jt += 2) {
         tile(Stage0{}, jt);
         if (jt + 1 < ntiles) tile(Stage1{}, jt + 1);
     }
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
 // Host-side launch; returns false if the launch itself failed.
 template <int D, int MT, int NW, int BN>
 inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
-                               int Hq, int Hkv, bool causal, float c_log2, uint16_t* out,
+                               int Hq, int Hkv, bool causal, int window, float c_log2, uint16_t* out,
                                hipStream_t stream) {
     const int gsize = Hq / Hkv;
     const int hw = gsize % 4 == 0 ? 4 : gsize % 2 == 0 ? 2 : 1;
@@ -385,16 +396,16 @@ inline bool launch_prefill_cfg(const uint16_t* q, const uint16_t* k, const uint1
     dim3 grid((unsigned)((int64_t)nbgh * nrb));
     dim3 block(64 * NW);
     hipLaunchKernelGGL((prefill_bf16<D, MT, NW, BN>), grid, block, 0, stream, q, k, v, P, Hq,
-                       Hkv, gsize, hw, nbgh, nrb, causal ? 1 : 0, c_log2, out);
+                       Hkv, gsize, hw, nbgh, nrb, causal ? 1 : 0, window, c_log2, out);
     return hipGetLastError() == hipSuccess;
 }
 
 inline bool launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int P,
-                           int Hq, int Hkv, int d, bool causal, float c_log2, uint16_t* out,
-                           hipStream_t stream) {
+                           int Hq, int Hkv, int d, bool causal, int window, float c_log2,
+                           uint16_t* out, hipStream_t stream) {
     if (d == 128)
-        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
-    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, c_log2, out, stream);
+        return launch_prefill_cfg<128, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, window, c_log2, out, stream);
+    return launch_prefill_cfg<64, kPrefillMT, kPrefillWaves, kPrefillBN>(q, k, v, B, P, Hq, Hkv, causal, window, c_log2, out, stream);
 }
 
 }  // namespace gqa

@@ -208,6 +208,16 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args *args, void *stream);
  * Only the shape, dtype, paging and num_splits fields are read. */
 gqa_status gqa_decode_ex_workspace_size(const gqa_decode_ex_args *args, size_t *bytes);
 
+/* Prefill with a sliding window: with causal != 0 and window W > 0, prompt
+ * position i attends to positions max(0, i - W + 1) .. i only (attention
+ * restricted to recent keys, "从MHA到GQA", section on what each
+ * attention-efficiency technique changes); W = 0 is gqa_prefill.  Same
+ * arguments and conventions as gqa_prefill otherwise; window > 0 without
+ * causal returns GQA_ERR_UNSUPPORTED, window < 0 GQA_ERR_SHAPE. */
+gqa_status gqa_prefill_ex(const void *q, const void *k, const void *v, int B, int P, int Hq,
+                          int Hkv, int d, int causal, int window, float scale, gqa_dtype dtype,
+                          void *out, void *stream);
+
 /* ------------------------------------------------------------------------
  * Counts (host only, exact integers).
  *

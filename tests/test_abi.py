@@ -228,3 +228,20 @@ def test_decode_ex_struct_layout_matches_header(tmp_path):
     assert int(got["sizeof"]) == ctypes.sizeof(DecodeExArgs)
     for f in fields:
         assert int(got[f]) == getattr(DecodeExArgs, f).offset, f
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(window=-1), Status.ERR_SHAPE),
+    (dict(window=16, causal=0), Status.ERR_UNSUPPORTED),
+    (dict(q=None), Status.ERR_NULL),
+    (dict(d=80), Status.ERR_HEADDIM),
+    (dict(dt=gqa.F32), Status.ERR_DTYPE),
+])
+def test_prefill_ex_validation(kw, expect):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, P=64, Hq=8, Hkv=2, d=128, causal=1, window=16,
+             scale=0.1, dt=gqa.BF16, out=FAKE, stream=None)
+    a.update(kw)
+    st = gqa.load().gqa_prefill_ex(a["q"], a["k"], a["v"], a["B"], a["P"], a["Hq"], a["Hkv"],
+                                   a["d"], a["causal"], a["window"], a["scale"], a["dt"], a["out"],
+                                   a["stream"])
+    assert st == expect

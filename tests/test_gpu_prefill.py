@@ -79,3 +79,43 @@ def test_prefill_rows_match_decode_on_gpu():
 def test_prefill_run_twice_bitwise():
     c = gi.prefill_case(1, 333, 16, 4, 128, "bf16", seed=99)
     assert np.array_equal(bits(run_prefill(c)), bits(run_prefill(c)))
+
+
+# --- sliding-window prefill (gqa_prefill_ex) --------------------------------
+# The oracle is the extended decode with one new token per prompt position
+# over the prompt's own K/V: token t sits at position t and sees the last
+# `window` keys up to it.
+
+def _window_ref(p, window, rows=None):
+    B, P = p.q.shape[:2]
+    return orc.decode_ex(p.q, p.k, p.v, np.full(B, P, np.int32), p.scale, window=window, rows=rows)
+
+
+@pytest.mark.parametrize("shape", [(2, 200, 8, 2, 128), (1, 97, 4, 4, 64), (2, 333, 16, 8, 128)])
+@pytest.mark.parametrize("window", [1, 7, 32, 63, 64, 65, 100, 1000])
+def test_window_prefill_small(shape, window):
+    B, P, Hq, Hkv, d = shape
+    p = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=70 + window)
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=window)
+    torch.cuda.synchronize()
+    ok, err = bf16_tol_ok(from_dev(out), _window_ref(p, window))
+    assert ok, err
+
+
+def test_window_prefill_full_size_sampled():
+    p = gi.prefill_case(2, 4096, 32, 8, 128, "bf16", seed=5)
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=1024)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(2 * 4096 * 32, 128, replace=False))
+    got = from_dev(out).reshape(-1, 128)[rows]
+    ok, err = bf16_tol_ok(got, _window_ref(p, 1024, rows=rows))
+    assert ok, err
+
+
+def test_window_at_least_prompt_is_plain_causal():
+    p = gi.prefill_case(1, 150, 8, 2, 128, "bf16", seed=79)
+    a = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale)
+    b = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=150)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
