@@ -381,7 +381,7 @@ gqa_status gqa_prefill_ex(const void* q, const void* k, const void* v, int B, in
     if (window > 0 && !causal) return GQA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * cdiv(P, gqa::kPrefillRows) > INT_MAX) return GQA_ERR_SHAPE;
     // byte offsets inside one sequence's K/V are 32-bit
-    if ((int64_t)(P + gqa::kPrefillBN) * Hkv * d * 2 > INT_MAX) return GQA_ERR_SHAPE;
+    if ((int64_t)(P + (4 * gqa::kPrefillChunk)) * Hkv * d * 2 > INT_MAX) return GQA_ERR_SHAPE;
     (void)hipGetLastError();
     if (!gqa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                              static_cast<const uint16_t*>(v), B, P, Hq, Hkv, d, causal != 0, window,
