@@ -215,8 +215,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int s = blockIdx.x % S;
-    const int bg = blockIdx.x / S;
+    // (b, KV head) varies fastest and the piece slowest: workgroups are dealt
+    // to the XCDs round-robin, so each XCD gets the same mix of pieces, and
+    // every first piece (always full) is dispatched before any later one.
+    const int nbg = gridDim.x / S;
+    const int s = blockIdx.x / nbg;
+    const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
     const int n = seqlens[b];
@@ -366,8 +370,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
     __shared__ float sm[MAXG], sl[MAXG], sa[MAXG];
 
     const int tid = threadIdx.x;
-    const int s = blockIdx.x % S;
-    const int bg = blockIdx.x / S;
+    // (b, KV head) varies fastest and the piece slowest: workgroups are dealt
+    // to the XCDs round-robin, so each XCD gets the same mix of pieces, and
+    // every first piece (always full) is dispatched before any later one.
+    const int nbg = gridDim.x / S;
+    const int s = blockIdx.x / nbg;
+    const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
     const int n = seqlens[b];
