@@ -146,6 +146,30 @@ def prefill_case(B, P, Hq, Hkv, d, dtype, seed, causal=True, scale=None,
     return PrefillCase(name, q, k, v, bool(causal), float(scale), dtype, dict(seed=seed))
 
 
+def prefill_growing_keys(B, P, Hq, Hkv, d, seed, profile, causal=True, name="prefill_growing") -> PrefillCase:
+    """Prefill inputs whose key rows grow in magnitude along the prompt, so a
+    row's largest score keeps rising and a lazily tracked softmax reference
+    must move many times (the plain draws settle it on the first keys).
+
+    profile: "linear" (key j scaled by 1 + 6 j / P), "exp" (by 2^(j / 96)), or
+    "jump" (keys from P/2 on scaled by 64).  The scaled rows are rounded back
+    to bf16; Q and V are the plain draws of prefill_case."""
+    c = prefill_case(B, P, Hq, Hkv, d, "bf16", seed, causal=causal, name=name)
+    j = np.arange(P, dtype=np.float64)
+    if profile == "linear":
+        f = 1.0 + 6.0 * j / P
+    elif profile == "exp":
+        f = np.exp2(j / 96.0)
+    elif profile == "jump":
+        f = np.where(j >= P // 2, 64.0, 1.0)
+    else:
+        raise ValueError(profile)
+    k32 = (c.k.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    k32 = (k32 * f[None, :, None, None]).astype(np.float32)
+    c.k[...] = bf16_bits_from_f32(k32)
+    return c
+
+
 # --------------------------------------------------------------------------
 # The five workloads.
 # --------------------------------------------------------------------------

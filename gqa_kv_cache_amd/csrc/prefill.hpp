@@ -62,16 +62,16 @@ constexpr float kRescaleSlack = 8.0f;              // log2 of the largest weight
 // gives factor 0 (or 1 while the row still has seen nothing).
 constexpr float kNoScoreYet = -3.4028234663852886e38f;
 
-// Position of 16-byte chunk c in K tile row r.  The 16 rows one operand
-// load reads per pass differ in bits {0,1,3,4} of r; the XOR spreads them
-// over all 64 banks: with 256-byte rows (16 chunks) those four bits pick the
-// chunk, with 128-byte rows bit 0 already picks the half of the banks and
-// bits {1,3,4} pick the chunk.  Bit 2 and bits above 4 are ignored, so rows
-// r + 4 and r + 32 share the pattern of row r.
+// Position of 16-byte piece c in row r of a staged K chunk.  The 16 rows one
+// operand load reads per pass differ in bits {0,1,3,4} of r; the XOR spreads
+// them over all 64 banks: with 256-byte rows (16 pieces) those four bits pick
+// the piece, with 128-byte rows bit 0 already picks the half of the banks and
+// bits {1,3,4} pick the piece.  Bit 2 is ignored, so the operand rows of the
+// second 16-key half (r + 4) share the pattern of the first.
 __device__ __forceinline__ int k_pos(int r, int c, int cpr) {
     return cpr == 16 ? c ^ (((r >> 1) & 0xC) | (r & 3)) : c ^ (((r >> 2) & 6) | ((r >> 1) & 1));
 }
-// Position of chunk c in V tile row r.  One transpose read serves 32 lanes
+// Position of piece c in row r of a staged V chunk.  One transpose read serves 32 lanes
 // per pass: rows 8g + 0..3 and 8g + 8..11.  The XOR with 2(r & 3) spreads
 // the four rows of one lane group over distinct banks; bit 3 of the row then
 // moves the second group onto the other half of the banks (an offset of 128

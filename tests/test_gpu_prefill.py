@@ -119,3 +119,30 @@ def test_window_at_least_prompt_is_plain_causal():
     b = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=150)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --- references that move along the prompt ----------------------------------
+# Key rows grow in magnitude along the prompt, so the running maximum of a
+# row's scores keeps rising and the kernel's lazily moved reference (an
+# integer, moved by an exact power-of-two rescale of O, the weight sums and
+# the weights already formed) is exercised on many chunks, for both halves of
+# a wave's row tiles, including a single large jump.
+
+@pytest.mark.parametrize("profile", ["linear", "exp", "jump"])
+@pytest.mark.parametrize("shape", [(1, 640, 8, 2, 128, True, 0), (2, 515, 12, 3, 64, True, 0),
+                                   (1, 700, 8, 8, 128, False, 0), (1, 600, 8, 2, 128, True, 200)])
+def test_prefill_moving_references(profile, shape):
+    B, P, Hq, Hkv, d, causal, window = shape
+    p = gi.prefill_growing_keys(B, P, Hq, Hkv, d, seed=120 + P, profile=profile, causal=causal)
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), causal, p.scale, window=window)
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    ref = _window_ref(p, window) if window else orc.prefill(p.q, p.k, p.v, causal, p.scale)
+    check("moving_%s" % profile, got, ref)
+
+
+def test_prefill_moving_references_negative_scale():
+    p = gi.prefill_growing_keys(1, 300, 8, 2, 128, seed=131, profile="linear")
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, -p.scale)
+    torch.cuda.synchronize()
+    check("moving_negative_scale", from_dev(out), orc.prefill(p.q, p.k, p.v, True, -p.scale))
