@@ -257,10 +257,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
         for (int e = 0; e < EPL; ++e) O[nt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int key0 = start + wave * kDecodeStep; key0 < end; key0 += kDecodeWaves * kDecodeStep) {
-        DecodeStepData<D> st;
-        decode_load_step<D>(st, kr, vr, rs2, key0, lane);
-        decode_compute_step<D, NT>(st, kt, key0, end, lane, c_log2, qB, O, m_run, l_run);
+    // The next step's rows are requested before this step is computed, so a
+    // wave's loads overlap its own compute.
+    constexpr int stride = kDecodeWaves * kDecodeStep;
+    int key0 = start + wave * kDecodeStep;
+    DecodeStepData<D> cur;
+    if (key0 < end) decode_load_step<D>(cur, kr, vr, rs2, key0, lane);
+    for (; key0 < end; key0 += stride) {
+        DecodeStepData<D> nxt;
+        if (key0 + stride < end) decode_load_step<D>(nxt, kr, vr, rs2, key0 + stride, lane);
+        decode_compute_step<D, NT>(cur, kt, key0, end, lane, c_log2, qB, O, m_run, l_run);
+        cur = nxt;
     }
 
     // Sum of weights across the four lane groups that share a head.
