@@ -211,6 +211,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     const int n0 = window > 0 ? max(0, iw - window + 1) / 32 : 0;
     const int n_end = (lim + 31) / 32;
     const bool active = iw < P && n0 < n_end;
+    // The step tests below are one unsigned range test each, on bounds fixed
+    // here: the wave works in steps [a_lo, a_lo + a_span) (from the empty
+    // chunk before its first one to its last one), and chunks
+    // [u_lo, u_lo + u_span] need no mask (whole rows inside the prompt, below
+    // the diagonal of every row of the wave and inside every row's window).
+    const int a_lo = n0 - 1;
+    const unsigned a_span = active ? (unsigned)max(0, min(n_end, c_hi) - a_lo) : 0u;
+    int u_hi = (P - 32) >> 5;
+    if (causal) u_hi = min(u_hi, (iw - 31) >> 5);
+    int u_lo = window > 0 ? ((wave_last_row - window) >> 5) + 1 : -(1 << 28);
+    if (u_hi < u_lo) u_lo = u_hi = 1 << 28;  // no such chunk
+    const unsigned u_span = (unsigned)(u_hi - u_lo);
     // Start loading chunk c of K or V into stage `stage`.  Each load gets a
     // buffer resource based at the chunk's first row; rows at or past P, and
     // chunks before the first or past the workgroup's last one, read as zero
@@ -247,9 +259,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
 
     // no row of the wave needs a mask in chunk n
     auto unmasked = [&](int n) __attribute__((always_inline)) -> bool {
-        const int j0 = 32 * n;
-        // bitwise, not short-circuit: one scalar condition, no branches
-        return (j0 + 32 <= P) & (!causal | (j0 + 31 <= iw)) & ((window <= 0) | (j0 > wave_last_row - window));
+        return (unsigned)(n - u_lo) <= u_span;
     };
     // Causal, window and tail mask of the chunk starting at key kc0.  Chunks
     // at or past n_end lie past every row's last key, so it removes them whole.
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         // visible since this barrier), read now so that step starts without
         // waiting for LDS.
         const char* kl_next = reinterpret_cast<const char*>(k_stage(IntC<(s_k + 1) & 3>{}));
-        if (__builtin_expect(!active | (n < n0 - 1) | (n >= n_end) | (n >= c_hi), 0)) {
+        if (__builtin_expect((unsigned)(n - a_lo) >= a_span, 0)) {
             kf_next[0] = kfrag(kl_next, 0);
             kf_next[1] = kfrag(kl_next, 1);
             return;
