@@ -10,7 +10,7 @@ import gqa_inputs as gi
 import gqa_kv_cache_amd as gqa
 from oracle import reference as orc
 from tests.gpu_util import bits, from_dev, to_dev
-from tests.helpers import bf16_tol_ok
+from tests.helpers import bf16_tol_ok, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,38 @@ def test_prefill_rows_match_decode_on_gpu():
 def test_prefill_run_twice_bitwise():
     c = gi.prefill_case(1, 333, 16, 4, 128, "bf16", seed=99)
     assert np.array_equal(bits(run_prefill(c)), bits(run_prefill(c)))
+
+
+def test_prefill_guard_bands_untouched():
+    """The kernel writes exactly the output rows: canaries around them survive."""
+    B, P, Hq, Hkv, d = 2, 203, 8, 2, 128
+    c = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=101)
+    n_out = B * P * Hq * d
+    guard = 4096
+    canary = 0x5A5A
+    out_big = torch.full((n_out + 2 * guard,), canary, dtype=torch.int16, device="cuda")
+    out = out_big[guard:guard + n_out].view(torch.bfloat16).view(B, P, Hq, d)
+    gqa.prefill(to_dev(c.q), to_dev(c.k), to_dev(c.v), causal=True, scale=c.scale, out=out)
+    torch.cuda.synchronize()
+    ob = out_big.cpu().numpy()
+    assert np.all(ob[:guard] == canary) and np.all(ob[guard + n_out:] == canary)
+    check("prefill_guarded", from_dev(out), orc.prefill(c.q, c.k, c.v, True, c.scale))
+
+
+@pytest.mark.parametrize("shape", [(1, 150, 8, 2, 128), (2, 77, 4, 4, 64)])
+def test_prefill_scale_zero_is_running_mean(shape):
+    """Scale 0 makes every visible key weigh the same: causal row i is the mean
+    of V rows 0..i of its group (a closed form, independent of the oracle)."""
+    B, P, Hq, Hkv, d = shape
+    c = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=103)
+    out = gqa.prefill(to_dev(c.q), to_dev(c.k), to_dev(c.v), causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    v = widen(c.v)                                   # [B, P, Hkv, d] exact
+    mean = np.cumsum(v, axis=1) / np.arange(1, P + 1)[None, :, None, None]
+    ref = np.repeat(mean, Hq // Hkv, axis=2)         # head h reads KV head h // (Hq/Hkv)
+    ok, err = bf16_tol_ok(got, ref)
+    assert ok, err
 
 
 # --- sliding-window prefill (gqa_prefill_ex) --------------------------------
