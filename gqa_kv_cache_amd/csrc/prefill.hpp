@@ -343,11 +343,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         // (K(n+2), V(n+1) and older; those of the previous barrier may still
         // fly); once every wave is here, they are visible to all, and nobody
         // reads K(n) or V(n-1) again.
-        // The waits are explicit (vmcnt(LPS), lgkmcnt(0)): a workgroup
+        // The waits are explicit (vmcnt(LPS), lgkmcnt(2)): a workgroup
         // fence would also wait for the direct loads still in flight.  The
-        // wavefront-scope fences emit nothing and only keep the compiler from
-        // moving LDS accesses across the barrier.
-        __builtin_amdgcn_s_waitcnt(0x0070 | LPS);
+        // two LDS reads allowed to fly are the last ones of the previous
+        // step, its prefetch of K(n+1), which no load started here
+        // overwrites; LDS reads complete in order, so every earlier read of
+        // K(n) and V(n-1) has completed.  The wavefront-scope fences emit
+        // nothing and only keep the compiler from moving LDS accesses across
+        // the barrier.
+        __builtin_amdgcn_s_waitcnt(0x0070 | LPS | (2 << 8));
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
