@@ -45,15 +45,12 @@ template <int D> struct VFragT;
 template <> struct VFragT<128> { typedef u32x4 T; };
 template <> struct VFragT<64> { typedef u32x2 T; };
 
-template <int D>
-__device__ __forceinline__ typename VFragT<D>::T load_vfrag(__amdgpu_buffer_rsrc_t r, int voff, int soff);
-template <>
-__device__ __forceinline__ u32x4 load_vfrag<128>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamLoad);
-}
-template <>
-__device__ __forceinline__ u32x2 load_vfrag<64>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamLoad);
+// POL is the cache policy of the loads: kStreamLoad when each row is read
+// once, 0 (cached) when several waves read the same rows.
+template <int D, int POL>
+__device__ __forceinline__ typename VFragT<D>::T load_vfrag(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (D == 128) return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL);
+    else return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL);
 }
 
 // One 32-key step of one wave, as loaded: K rows (row pattern: each load
@@ -63,7 +60,7 @@ template <int D> struct DecodeStepData {
     typename VFragT<D>::T vB[2][4];
 };
 
-template <int D>
+template <int D, int POL = kStreamLoad>
 __device__ __forceinline__ void decode_load_step(DecodeStepData<D>& st, __amdgpu_buffer_rsrc_t kr,
                                                  __amdgpu_buffer_rsrc_t vr, int rs2, int key0,
                                                  int lane) {
@@ -72,12 +69,12 @@ __device__ __forceinline__ void decode_load_step(DecodeStepData<D>& st, __amdgpu
     const int vk = (key0 + lane / Sh::CPR) * rs2 + 16 * (lane % Sh::CPR);
 #pragma unroll
     for (int i = 0; i < Sh::KLD; ++i)
-        st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, vk, Sh::RPI * i * rs2, kStreamLoad);
+        st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, vk, Sh::RPI * i * rs2, POL);
     const int vv = (key0 + 4 * grp) * rs2 + 2 * Sh::EPL * col;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st.vB[t][r] = load_vfrag<D>(vr, vv, (16 * t + r) * rs2);
+        for (int r = 0; r < 4; ++r) st.vB[t][r] = load_vfrag<D, POL>(vr, vv, (16 * t + r) * rs2);
 }
 
 // Consume one step: K rows go through the wave's LDS tile (XOR-swizzled by
@@ -350,6 +347,115 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
             if (c == 0) {
                 ws_ml[(row * S + s) * 2] = sm_m[h];
                 ws_ml[(row * S + s) * 2 + 1] = sm_l[h];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 split kernel for groups of 49..64 query heads (four 16-head tiles).
+//
+// Each of the four waves owns one tile of heads and streams every row of the
+// piece itself, with the same step as decode_split_bf16, so no partial
+// results are combined across waves.  The four waves read the same rows at
+// about the same time; their loads go through L2 (default cache policy),
+// which serves the repeats, so memory still supplies each row once.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16_tiles(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ seqlens, int Hq, int Hkv,
+    int Lmax, int gsize, int S, int chunk, float c_log2, uint16_t* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    typedef DecodeShape<D> Sh;
+    constexpr int KI = Sh::KI;
+    constexpr int EPL = Sh::EPL;
+    static_assert(kDecodeWaves == 4, "one 16-head tile per wave");
+
+    __shared__ u32x4 k_tiles[kDecodeWaves][32 * Sh::CPR];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int nbg = gridDim.x / S;
+    const int s = blockIdx.x / nbg;
+    const int bg = blockIdx.x % nbg;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int n = seqlens[b];
+    const int start = s * chunk;
+    const int end = min(start + chunk, n);
+    if (S > 1 && start >= end) return;  // empty split: the merge skips it
+
+    const int rs2 = Hkv * D * 2;
+    const uint16_t* kb = kc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const uint16_t* vb = vc + ((int64_t)b * Lmax * Hkv + g) * D;
+    const int valid_bytes = end > 0 ? (end - 1) * rs2 + D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, valid_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, valid_bytes);
+    u32x4* kt = k_tiles[wave];
+    const int h0 = g * gsize;
+    const int ht = 16 * wave;  // first head of this wave's tile, within the group
+
+    bf16x8 qB[1][KI];
+    {
+        const int hq = ht + col;
+        const bool ok = hq < gsize;
+        const uint16_t* qp = q + ((int64_t)b * Hq + h0 + (ok ? hq : 0)) * D + 8 * grp;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) qB[0][i] = as_bf16x8(load16(qp + 32 * i, ok));
+    }
+    f32x4 O[1][EPL];
+    float m_run[1] = {kNegInf}, l_run[1] = {0.f};
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[0][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int key0 = start;
+    DecodeStepData<D> cur;
+    if (key0 < end) decode_load_step<D, 0>(cur, kr, vr, rs2, key0, lane);
+    for (; key0 < end; key0 += kDecodeStep) {
+        DecodeStepData<D> nxt;
+        if (key0 + kDecodeStep < end) decode_load_step<D, 0>(nxt, kr, vr, rs2, key0 + kDecodeStep, lane);
+        decode_compute_step<D, 1>(cur, kt, key0, end, lane, c_log2, qB, O, m_run, l_run);
+        cur = nxt;
+    }
+
+    // Sum of weights across the four lane groups that share a head (lane col
+    // holds head ht + col); O row r of lane (col, grp) is head ht + 4grp + r.
+    float l = l_run[0];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    float lr[4], mr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        lr[r] = __shfl(l, 4 * grp + r);
+        mr[r] = __shfl(m_run[0], 4 * grp + r);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = ht + 4 * grp + r;
+        if (h >= gsize) continue;
+        const int64_t row = (int64_t)b * Hq + h0 + h;
+        if (S == 1) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < EPL / 2; ++j) {
+                const float x0 = lr[r] > 0.f ? O[0][2 * j][r] / lr[r] : 0.f;
+                const float x1 = lr[r] > 0.f ? O[0][2 * j + 1][r] / lr[r] : 0.f;
+                o[j] = pack_bf16x2_rne(x0, x1);
+            }
+            uint16_t* dst = out + row * D + EPL * col;
+            if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(dst) = o;
+            else *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
+        } else {
+            float* dst = ws_acc + (row * S + s) * D + EPL * col;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<f32x4*>(dst + e) = f32x4{O[0][e][r], O[0][e + 1][r], O[0][e + 2][r], O[0][e + 3][r]};
+            if (col == 0) {
+                ws_ml[(row * S + s) * 2] = mr[r];
+                ws_ml[(row * S + s) * 2 + 1] = lr[r];
             }
         }
     }
