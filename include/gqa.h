@@ -125,7 +125,8 @@ gqa_status gqa_decode_workspace_size(int B, int Hq, int Hkv, int d, int Lmax, gq
  *   out  [B, P, Hq, d]
  *   dtype  GQA_BF16 only (the matrix-core path); GQA_F32 -> GQA_ERR_DTYPE
  *   d      64 or 128;  1 <= Hq/Hkv <= 64;  B, P, Hq, Hkv >= 1;
- *          (P + 64) * Hkv * d * 2 must not exceed 2^31 - 1
+ *          (P + 128) * Hkv * d * 2 must not exceed 2^31 - 1 (K/V chunk byte
+ *          offsets are 32-bit), else GQA_ERR_SHAPE
  *
  * Returns GQA_OK or an error code; see the conventions above.
  * ------------------------------------------------------------------------ */

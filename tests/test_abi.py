@@ -76,6 +76,9 @@ def _decode(**kw):
     (dict(ns=4, ws=None), Status.ERR_WORKSPACE),
     (dict(ns=4, ws=FAKE, wsb=16), Status.ERR_WORKSPACE),
     (dict(ns=4, ws=FAKE + 4, wsb=1 << 30), Status.ERR_WORKSPACE),
+    # one sequence's cache slice is addressed with 32-bit byte offsets:
+    # (Lmax + 32) * Hkv * d * 4 = 2097153 * 1024 > 2^31 - 1
+    (dict(Lmax=2097121), Status.ERR_SHAPE),
 ])
 def test_decode_validation(kw, expect):
     assert _decode(**kw) == expect
@@ -97,6 +100,8 @@ def _prefill(**kw):
     (dict(d=32), Status.ERR_HEADDIM),
     (dict(dt=gqa.F32), Status.ERR_DTYPE),
     (dict(Hq=65 * 2, Hkv=2), Status.ERR_UNSUPPORTED),
+    # K/V chunk byte offsets are 32-bit: (P + 128) * Hkv * d * 2 = 2^31 > 2^31 - 1
+    (dict(P=4194176), Status.ERR_SHAPE),
 ])
 def test_prefill_validation(kw, expect):
     assert _prefill(**kw) == expect
