@@ -118,6 +118,18 @@ def test_shapes_ragged_nan_poisoned(dtype, d, Hq, Hkv, splits):
     assert np.all(got[0] == 0.0)  # zero-length sequence
 
 
+@pytest.mark.parametrize("G,Hkv", [(49, 1), (56, 2), (63, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_partial_last_head_tile(G, Hkv, d, splits):
+    """Groups of 49..63 heads: four 16-head tiles, the last one partly empty."""
+    c = gi.decode_case(len(SEQ), G * Hkv, Hkv, d, 300, SEQ, "bf16", q_seed=G + d, kv_seed=G + splits,
+                       invalid="nan", name="partial_tile_G%d_Hkv%d_d%d_s%d" % (G, Hkv, d, splits))
+    got = from_dev(run_decode(c, splits))
+    check(c, got, orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
+    assert np.all(got[0] == 0.0)  # zero-length sequence
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 0])
 def test_long_two_sequences(splits):
     c = gi.decode_case(2, 16, 2, 128, 4096, [4096, 4000], "bf16", q_seed=5, kv_seed=6, invalid="nan")
