@@ -107,12 +107,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     constexpr int SL2 = MT * NB + MT;  // matrix-core slots of phase 2
     constexpr int NWT = 8 * HA;        // weights per lane formed in each phase
     constexpr int SC = 4;              // phase-2 slots before the reference check
-    // 1 KB loads per wave and chunk: each operand's chunk is CS / 64 blocks,
-    // spread over the waves; with one load per wave, the first half of the
-    // waves moves K and the second half V.
+    // 1 KB loads per chunk: each operand's chunk is CS / 64 blocks.  With one
+    // load per wave the first half of the waves moves K and the second half
+    // V; with more, the first half moves both.  On each SIMD the wave of the
+    // second half is the one that waits for the matrix cores (the older wave
+    // wins them), so the issue work goes to the first.
     constexpr int LPS = CS / 64 * 2 / NW;
     static_assert(LPS >= 1 && (LPS == 1 || LPS % 2 == 0) && LPS * NW == CS / 64 * 2, "chunk blocks split evenly over the waves");
-    constexpr int BPO = LPS == 1 ? 1 : LPS / 2;  // blocks per operand and wave
+    constexpr int BPO = LPS == 1 ? 1 : LPS;  // blocks per operand and loading wave
     // Four LDS objects; object x holds K stage x and V stage x-1 (mod 4).
     // Step n reads K(n+1) and V(n), both in one object, and every direct
     // load still in flight then targets one of the other three: distinct
@@ -189,14 +191,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         for (int e = 0; e < NB; ++e)
             vt_byte[e] = r * CPR * 16 + v_pos(r, 2 * e + (m >> 1), CPR) * 16 + 8 * (m & 1);
     }
-    // Chunk fill: this wave moves BPO 1 KB blocks (64 lanes x 16 bytes) of
-    // K and of V, blocks wave, wave + NW, ... (with one load per wave: block
-    // wave mod NW/2 of K or of V).  Lane l of block blk lands in slot
-    // 64*blk + l and fetches the piece the swizzle places there.
+    // Chunk fill: a wave of the first half moves BPO 1 KB blocks (64 lanes x
+    // 16 bytes) of K and of V, blocks wave, wave + NW/2, ... (with one load
+    // per wave: every wave moves block wave mod NW/2 of K or of V).  Lane l
+    // of block blk lands in slot 64*blk + l and fetches the piece the
+    // swizzle places there.
     int blk[BPO], k_off[BPO], v_off[BPO];
 #pragma unroll
     for (int x = 0; x < BPO; ++x) {
-        blk[x] = LPS == 1 ? wave % (NW / 2) : wave + NW * x;
+        blk[x] = LPS == 1 ? wave % (NW / 2) : (wave % (NW / 2)) + (NW / 2) * x;
         const int slot = 64 * blk[x] + lane;
         const int r = slot / CPR, pos = slot % CPR;
         k_off[x] = r * ks2 + 16 * k_pos(r, pos, CPR);
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     // chunks before the first or past the workgroup's last one, read as zero
     // without touching memory.
     auto fill_k = [&](auto stage, int c) __attribute__((always_inline)) {
-        if (LPS == 1 && wave >= NW / 2) return;
+        if (wave >= NW / 2) return;
         const int base = 32 * min(max(c, 0), c_hi) * ks2;
         const int nrec = c >= 0 && c < c_hi ? valid_bytes - base : 0;
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb + base), (short)0, nrec, 0x00020000);
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&k_stage(stage)[64 * blk[x]], 16u, (unsigned)k_off[x], 0u, 0u, 0u);
     };
     auto fill_v = [&](auto stage, int c) __attribute__((always_inline)) {
-        if (LPS == 1 && wave < NW / 2) return;
+        if (LPS == 1 ? wave < NW / 2 : wave >= NW / 2) return;
         const int base = 32 * min(max(c, 0), c_hi) * ks2;
         const int nrec = c >= 0 && c < c_hi ? valid_bytes - base : 0;
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb + base), (short)0, nrec, 0x00020000);
@@ -339,11 +342,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
     auto step = [&](auto S, int n) __attribute__((always_inline)) {
         constexpr int s_v = decltype(S)::value;
         constexpr int s_k = (s_v + 1) & 3;
-        // This wave's loads up to the one two barriers back have landed
+        // This wave's loads up to the ones two barriers back have landed
         // (K(n+2), V(n+1) and older; those of the previous barrier may still
         // fly); once every wave is here, they are visible to all, and nobody
         // reads K(n) or V(n-1) again.
-        // The waits are explicit (vmcnt(LPS), lgkmcnt(2)): a workgroup
+        // The waits are explicit (vmcnt: the loads of one barrier may fly;
+        // lgkmcnt(2)): a workgroup
         // fence would also wait for the direct loads still in flight.  The
         // two LDS reads allowed to fly are the last ones of the previous
         // step, its prefetch of K(n+1), which no load started here
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_bf16(
         // K(n) and V(n-1) has completed.  The wavefront-scope fences emit
         // nothing and only keep the compiler from moving LDS accesses across
         // the barrier.
-        __builtin_amdgcn_s_waitcnt(0x0070 | LPS | (2 << 8));
+        __builtin_amdgcn_s_waitcnt(0x0070 | (LPS == 1 ? 1 : 2 * LPS) | (2 << 8));
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
