@@ -238,8 +238,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     constexpr int HT = 16 * NT;
 
     __shared__ float sm_o[HT * D];
-    __shared__ float sm_m[HT];
-    __shared__ float sm_l[HT];
+    __shared__ float sm_m[HT > 16 ? HT : 16 * NWV];
+    __shared__ float sm_l[HT > 16 ? HT : 16 * NWV];
     __shared__ u32x4 k_tiles[NWV][32 * Sh::CPR];
 
     const int lane = threadIdx.x & 63;
@@ -341,6 +341,67 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
         l_run[nt] += __shfl_xor(l_run[nt], 16);
         l_run[nt] += __shfl_xor(l_run[nt], 32);
     }
+    const float vsc = KV8 ? v_scale[g] : 1.f;
+    constexpr int C8 = D / 8;
+    const int items = R * C8;
+    if constexpr (NT == 1) {
+        // One tile: each wave's partial result (16 rows x D floats) fits in
+        // its own K tile, which it no longer reads.  Every wave stores its
+        // part, and after one barrier every thread combines one (row, 8
+        // head-dim values) piece over the waves.
+        float* part = reinterpret_cast<float*>(kt);
+        static_assert(16 * D * sizeof(float) <= 32 * Sh::CPR * sizeof(u32x4), "partial fits the K tile");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * grp + r;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<f32x4*>(part + h * D + EPL * col + e) =
+                    f32x4{O[0][e][r], O[0][e + 1][r], O[0][e + 2][r], O[0][e + 3][r]};
+        }
+        if (grp == 0) {
+            sm_m[wave * 16 + col] = m_run[0];
+            sm_l[wave * 16 + col] = l_run[0];
+        }
+        __syncthreads();
+        for (int it = threadIdx.x; it < items; it += 64 * NWV) {
+            const int h = it / C8;
+            const int c = (it % C8) * 8;
+            const int t = h / gsize, hh = h % gsize;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+            float L = 0.f;
+            f32x4 o0 = f32x4{0.f, 0.f, 0.f, 0.f}, o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) {
+                const float f = M == kNegInf ? 0.f : fast_exp2(sm_m[w * 16 + h] - M);
+                L += f * sm_l[w * 16 + h];
+                const float* src = reinterpret_cast<const float*>(k_tiles[w]) + h * D + c;
+                o0 += f * *reinterpret_cast<const f32x4*>(src);
+                o1 += f * *reinterpret_cast<const f32x4*>(src + 4);
+            }
+            const int64_t row = ((int64_t)b * T + t) * Hq + h0 + hh;
+            if (S == 1) {
+                const float f = L > 0.f ? vsc / L : 0.f;
+                u32x4 o;
+                o[0] = pack_bf16x2_rne(o0[0] * f, o0[1] * f);
+                o[1] = pack_bf16x2_rne(o0[2] * f, o0[3] * f);
+                o[2] = pack_bf16x2_rne(o1[0] * f, o1[1] * f);
+                o[3] = pack_bf16x2_rne(o1[2] * f, o1[3] * f);
+                *reinterpret_cast<u32x4*>(out + row * D + c) = o;
+            } else {
+                float* dst = ws_acc + (row * S + s) * D + c;
+                *reinterpret_cast<f32x4*>(dst) = o0 * vsc;
+                *reinterpret_cast<f32x4*>(dst + 4) = o1 * vsc;
+                if (c == 0) {
+                    ws_ml[(row * S + s) * 2] = M;
+                    ws_ml[(row * S + s) * 2 + 1] = L;
+                }
+            }
+        }
+        return;
+    }
     // Combine the waves of the workgroup in LDS, one wave at a time.
     if (wave == 0) {
 #pragma unroll
@@ -390,9 +451,6 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     }
     __syncthreads();
 
-    const float vsc = KV8 ? v_scale[g] : 1.f;
-    constexpr int C8 = D / 8;
-    const int items = R * C8;
     for (int it = threadIdx.x; it < items; it += 64 * NWV) {
         const int h = it / C8;
         const int c = (it % C8) * 8;
