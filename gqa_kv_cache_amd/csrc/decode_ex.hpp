@@ -235,11 +235,9 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     typedef ExShape<D, KV8> Ex;
     constexpr int KI = Sh::KI;
     constexpr int EPL = Sh::EPL;
-    constexpr int HT = 16 * NT;
 
-    __shared__ float sm_o[HT * D];
-    __shared__ float sm_m[HT > 16 ? HT : 16 * NWV];
-    __shared__ float sm_l[HT > 16 ? HT : 16 * NWV];
+    __shared__ float sm_m[16 * NWV];  // per wave: running max of each row of a tile
+    __shared__ float sm_l[16 * NWV];  // per wave: weight sum of each row of a tile
     __shared__ u32x4 k_tiles[NWV][32 * Sh::CPR];
 
     const int lane = threadIdx.x & 63;
@@ -342,42 +340,45 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
         l_run[nt] += __shfl_xor(l_run[nt], 32);
     }
     const float vsc = KV8 ? v_scale[g] : 1.f;
+    // Combine the waves' partial results, one 16-row tile at a time: each
+    // wave's part of the tile (16 rows x D floats) is staged in its own K
+    // tile, which it no longer reads, and after a barrier every thread
+    // combines one (row, 8 head-dim values) piece over the waves.
+    float* part = reinterpret_cast<float*>(kt);
+    static_assert(16 * D * sizeof(float) <= 32 * Sh::CPR * sizeof(u32x4), "a tile's part fits the K tile");
     constexpr int C8 = D / 8;
-    const int items = R * C8;
-    if constexpr (NT == 1) {
-        // One tile: each wave's partial result (16 rows x D floats) fits in
-        // its own K tile, which it no longer reads.  Every wave stores its
-        // part, and after one barrier every thread combines one (row, 8
-        // head-dim values) piece over the waves.
-        float* part = reinterpret_cast<float*>(kt);
-        static_assert(16 * D * sizeof(float) <= 32 * Sh::CPR * sizeof(u32x4), "partial fits the K tile");
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (nt > 0) __syncthreads();  // the previous tile's parts have been read
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int h = 4 * grp + r;
 #pragma unroll
             for (int e = 0; e < EPL; e += 4)
                 *reinterpret_cast<f32x4*>(part + h * D + EPL * col + e) =
-                    f32x4{O[0][e][r], O[0][e + 1][r], O[0][e + 2][r], O[0][e + 3][r]};
+                    f32x4{O[nt][e][r], O[nt][e + 1][r], O[nt][e + 2][r], O[nt][e + 3][r]};
         }
         if (grp == 0) {
-            sm_m[wave * 16 + col] = m_run[0];
-            sm_l[wave * 16 + col] = l_run[0];
+            sm_m[wave * 16 + col] = m_run[nt];
+            sm_l[wave * 16 + col] = l_run[nt];
         }
         __syncthreads();
+        const int items = min(16, R - 16 * nt) * C8;
         for (int it = threadIdx.x; it < items; it += 64 * NWV) {
-            const int h = it / C8;
+            const int i = it / C8;
             const int c = (it % C8) * 8;
+            const int h = 16 * nt + i;
             const int t = h / gsize, hh = h % gsize;
             float M = kNegInf;
 #pragma unroll
-            for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+            for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w * 16 + i]);
             float L = 0.f;
             f32x4 o0 = f32x4{0.f, 0.f, 0.f, 0.f}, o1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < NWV; ++w) {
-                const float f = M == kNegInf ? 0.f : fast_exp2(sm_m[w * 16 + h] - M);
-                L += f * sm_l[w * 16 + h];
-                const float* src = reinterpret_cast<const float*>(k_tiles[w]) + h * D + c;
+                const float f = M == kNegInf ? 0.f : fast_exp2(sm_m[w * 16 + i] - M);
+                L += f * sm_l[w * 16 + i];
+                const float* src = reinterpret_cast<const float*>(k_tiles[w]) + i * D + c;
                 o0 += f * *reinterpret_cast<const f32x4*>(src);
                 o1 += f * *reinterpret_cast<const f32x4*>(src + 4);
             }
@@ -398,79 +399,6 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
                     ws_ml[(row * S + s) * 2] = M;
                     ws_ml[(row * S + s) * 2 + 1] = L;
                 }
-            }
-        }
-        return;
-    }
-    // Combine the waves of the workgroup in LDS, one wave at a time.
-    if (wave == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int h = 16 * nt + 4 * grp + r;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) sm_o[h * D + EPL * col + e] = O[nt][e][r];
-            }
-            if (grp == 0) {
-                sm_m[16 * nt + col] = m_run[nt];
-                sm_l[16 * nt + col] = l_run[nt];
-            }
-        }
-    }
-    for (int w = 1; w < NWV; ++w) {
-        __syncthreads();
-        if (wave == w) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int h = 16 * nt + 4 * grp + r;
-                    const float mo = sm_m[h];
-                    const float mw = __shfl(m_run[nt], 4 * grp + r);
-                    const float M = fmaxf(mo, mw);
-                    const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
-                    const float fb = M == kNegInf ? 0.f : fast_exp2(mw - M);
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) {
-                        const int idx = h * D + EPL * col + e;
-                        sm_o[idx] = fa * sm_o[idx] + fb * O[nt][e][r];
-                    }
-                }
-                const float mo = sm_m[16 * nt + col];
-                const float lw = sm_l[16 * nt + col];
-                const float M = fmaxf(mo, m_run[nt]);
-                const float fa = M == kNegInf ? 0.f : fast_exp2(mo - M);
-                const float fb = M == kNegInf ? 0.f : fast_exp2(m_run[nt] - M);
-                if (grp == 0) {
-                    sm_m[16 * nt + col] = M;
-                    sm_l[16 * nt + col] = fa * lw + fb * l_run[nt];
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    for (int it = threadIdx.x; it < items; it += 64 * NWV) {
-        const int h = it / C8;
-        const int c = (it % C8) * 8;
-        const int t = h / gsize, hh = h % gsize;
-        const float* src = sm_o + h * D + c;
-        const int64_t row = ((int64_t)b * T + t) * Hq + h0 + hh;
-        if (S == 1) {
-            const float l = sm_l[h];
-            const float f = l > 0.f ? vsc / l : 0.f;
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2_rne(src[2 * j] * f, src[2 * j + 1] * f);
-            *reinterpret_cast<u32x4*>(out + row * D + c) = o;
-        } else {
-            float* dst = ws_acc + (row * S + s) * D + c;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{src[0] * vsc, src[1] * vsc, src[2] * vsc, src[3] * vsc};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4] * vsc, src[5] * vsc, src[6] * vsc, src[7] * vsc};
-            if (c == 0) {
-                ws_ml[(row * S + s) * 2] = sm_m[h];
-                ws_ml[(row * S + s) * 2 + 1] = sm_l[h];
             }
         }
     }
