@@ -170,9 +170,10 @@ def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
         vs.append(vs[0].clone())
     sl = torch.from_numpy(case.seqlens).cuda()
     kw = {}
-    if case.kv == "fp8":
+    if case.kv_format:
         kw["k_scale"] = torch.from_numpy(case.k_scale).cuda()
         kw["v_scale"] = torch.from_numpy(case.v_scale).cuda()
+        kw["kv_format"] = case.kv_format
     if case.block_table is not None:
         kw["block_table"] = torch.from_numpy(case.block_table).cuda()
         kw["block_size"] = case.block_size
@@ -186,14 +187,14 @@ def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
     wall_ms, ev_ms, per_call = time_calls(fn, steps, warmup, torch, rotate=copies)
     B, T, Hq, d = case.q.shape
     Hkv = case.k.shape[2]
-    elt = 1 if case.kv == "fp8" else 2
+    elt = 1 if case.kv_format else 2
     # rows some token of the sequence can see, read once per KV head; q and out
     first = [max(0, int(n) - T - case.window + 1) if case.window > 0 else 0 for n in case.seqlens]
     rows = sum(int(n) - f for n, f in zip(case.seqlens, first))
     nbytes = rows * 2 * Hkv * d * elt + 2 * B * T * Hq * d * 2
     us = ev_ms * 1e3
     del ks, vs
-    return {"workload": case.name, "T": T, "kv_dtype": "e4m3" if case.kv == "fp8" else "bf16",
+    return {"workload": case.name, "T": T, "kv_dtype": case.kv_format or "bf16",
             "paged_block_size": case.block_size or None, "window": case.window or None,
             "bytes": nbytes, "us_per_step": us, "us_per_call_median": median(per_call) * 1e3,
             "achieved_TBps": nbytes / (us * 1e-6) / 1e12,
@@ -353,6 +354,7 @@ def main():
                    invalid="zero")
         variants = [
             ("decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096", dict(kv="fp8")),
+            ("decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096", dict(kv="e5m2")),
             ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4)),
             ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64)),
             ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),

@@ -221,6 +221,7 @@ def prefill_causal() -> PrefillCase:
 
 TAG_KNEW, TAG_VNEW, TAG_SCALE, TAG_PERM = 4, 5, 6, 7
 NAN_E4M3 = np.uint8(0x7F)
+NAN_E5M2 = np.uint8(0x7F)      # S.11111.11: a NaN in E5M2 as well
 
 
 def _draw_e4m3(seed_words, shape) -> np.ndarray:
@@ -231,6 +232,19 @@ def _draw_e4m3(seed_words, shape) -> np.ndarray:
     expo = rng.integers(3, 11, shape, dtype=np.uint8) << np.uint8(3)
     mant = rng.integers(0, 8, shape, dtype=np.uint8)
     return (sign | expo | mant).astype(np.uint8)
+
+
+def _draw_e5m2(seed_words, shape) -> np.ndarray:
+    """Random OCP E5M2 codes: random sign and mantissa, exponent field drawn
+    from 11..18 (magnitudes 2^-4 .. 14), so no infinity, NaN or subnormal."""
+    rng = np.random.default_rng(list(seed_words))
+    sign = rng.integers(0, 2, shape, dtype=np.uint8) << np.uint8(7)
+    expo = rng.integers(11, 19, shape, dtype=np.uint8) << np.uint8(2)
+    mant = rng.integers(0, 4, shape, dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
+
+
+FP8_KINDS = {"fp8": "e4m3", "e5m2": "e5m2"}   # case kind -> FP8 format of its byte rows
 
 
 @dataclass
@@ -246,8 +260,8 @@ class DecodeExCase:
     seqlens: np.ndarray      # [B] int32, counts the T new tokens
     scale: float
     dtype: str               # q/out dtype: "f32" or "bf16"
-    kv: str                  # "same" (q's dtype) or "fp8"
-    k_scale: np.ndarray = None   # [Hkv] float32 (fp8 only)
+    kv: str                  # "same" (q's dtype), "fp8" (E4M3 bytes) or "e5m2" (E5M2 bytes)
+    k_scale: np.ndarray = None   # [Hkv] float32 (FP8 kinds only)
     v_scale: np.ndarray = None
     block_table: np.ndarray = None   # [B, max_blocks] int32 (paged only)
     block_size: int = 0
@@ -258,24 +272,33 @@ class DecodeExCase:
     def T(self):
         return self.q.shape[1]
 
+    @property
+    def kv_format(self):
+        """FP8 format of the byte rows ("e4m3" / "e5m2"), None for q's dtype."""
+        return FP8_KINDS.get(self.kv)
+
 
 def decode_ex_case(B, T, Hq, Hkv, d, Lmax, seqlens, dtype, seed, kv="same", paged=False,
                    block_size=64, window=0, invalid="nan", scale=None,
                    name="decode_ex") -> DecodeExCase:
     """q from [seed, 1]; cached rows of sequence b from [seed, 2|3, b]; the T
     new rows from [seed, 4|5]; FP8 per-head scales from [seed, 6]; the block
-    permutation of a paged pool from [seed, 7]."""
+    permutation of a paged pool from [seed, 7].  kv: "same", "fp8" (E4M3
+    bytes) or "e5m2" (E5M2 bytes)."""
     seqlens = np.asarray(seqlens, dtype=np.int32)
     assert seqlens.shape == (B,) and int(seqlens.min()) >= T and int(seqlens.max()) <= Lmax
-    fp8 = kv == "fp8"
+    assert kv in ("same", "fp8", "e5m2")
+    fp8 = kv != "same"
     st = np.uint8 if fp8 else _storage(dtype)
 
     def rows(words, shape):
+        if kv == "e5m2":
+            return _draw_e5m2(words, shape)
         return _draw_e4m3(words, shape) if fp8 else _draw(words, shape, dtype)
 
     def poison(a):
         if fp8:
-            a[...] = NAN_E4M3 if invalid == "nan" else 0
+            a[...] = (NAN_E5M2 if kv == "e5m2" else NAN_E4M3) if invalid == "nan" else 0
         else:
             _fill_invalid(a, dtype, invalid)
 

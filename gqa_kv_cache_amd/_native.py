@@ -16,7 +16,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libgqa.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
 
 
 class Status(enum.IntEnum):
@@ -190,25 +190,41 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, wor
     return out
 
 
-def _kv_code(t) -> int:
+_FP8_FORMATS = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
+
+
+def _kv_code(t, kv_format) -> int:
+    """Cache element code: bfloat16, or FP8 bytes named by their torch dtype
+    (float8_e4m3fn / float8_e5m2) or, for uint8, by ``kv_format``."""
     import torch
+    if kv_format is not None and kv_format not in _FP8_FORMATS:
+        raise ValueError("gqa: kv_format must be 'e4m3' or 'e5m2'")
     if t.dtype == torch.bfloat16:
+        if kv_format is not None:
+            raise TypeError("gqa: kv_format names the format of FP8 caches only")
         return BF16
-    if t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None):
-        return FP8_E4M3
-    raise TypeError("gqa: KV cache must be bfloat16, or E4M3 bytes (uint8 / float8_e4m3fn)")
+    named = {getattr(torch, "float8_e4m3fn", None): FP8_E4M3,
+             getattr(torch, "float8_e5m2", None): FP8_E5M2}.get(t.dtype)
+    if named is not None:
+        if kv_format is not None and _FP8_FORMATS[kv_format] != named:
+            raise TypeError("gqa: kv_format disagrees with the cache dtype")
+        return named
+    if t.dtype == torch.uint8:
+        return _FP8_FORMATS[kv_format or "e4m3"]
+    raise TypeError("gqa: KV cache must be bfloat16, or FP8 bytes (float8_e4m3fn, float8_e5m2, "
+                    "or uint8 with kv_format)")
 
 
 def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale=None,
               block_table=None, block_size=0, window=0, k_new=None, v_new=None, out=None,
-              num_splits=0, workspace=None):
+              num_splits=0, workspace=None, kv_format=None):
     """Extended decode step (gqa_decode_ex).
 
     q [B,T,Hq,d] bfloat16; seqlens [B] int32 counts the T new tokens.
     k_cache, v_cache: contiguous [B,Lmax,Hkv,d] or, with ``block_table``
     [B,max_blocks] int32, a pool [num_blocks,block_size,Hkv,d]; bfloat16 or
-    E4M3 bytes (uint8 / float8_e4m3fn) with ``k_scale``, ``v_scale`` [Hkv]
-    float32.  ``k_new``/``v_new`` [B,T,Hkv,d] (cache dtype) are stored into the
+    FP8 bytes with ``k_scale``, ``v_scale`` [Hkv] float32: float8_e4m3fn /
+    float8_e5m2, or uint8 in ``kv_format`` ("e4m3", the default, or "e5m2").  ``k_new``/``v_new`` [B,T,Hkv,d] (cache dtype) are stored into the
     cache first when given.  ``window`` > 0 keeps the last ``window`` keys of
     each token.  Returns ``out`` [B,T,Hq,d] bfloat16.
     """
@@ -226,7 +242,7 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
         raise ValueError("gqa: inconsistent shapes")
     if q.dtype != torch.bfloat16:
         raise TypeError("gqa: q must be bfloat16")
-    kv = _kv_code(k_cache)
+    kv = _kv_code(k_cache, kv_format)
     if v_cache.dtype != k_cache.dtype:
         raise TypeError("gqa: k_cache and v_cache must share one dtype")
     a = DecodeExArgs()
@@ -243,7 +259,7 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
         max_blocks, num_blocks = block_table.shape[1], k_cache.shape[0]
         Lmax = max_blocks * block_size
         a.block_table = block_table.data_ptr()
-    if kv == FP8_E4M3:
+    if kv != BF16:
         if k_scale is None or v_scale is None:
             raise ValueError("gqa: FP8 caches need k_scale and v_scale")
         for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):

@@ -1,5 +1,5 @@
 // Extended GQA decode for gfx950: several new query tokens per sequence, an
-// optional sliding window, a paged cache and an FP8 (OCP E4M3) cache.
+// optional sliding window, a paged cache and an FP8 (OCP E4M3 or E5M2) cache.
 //
 // Same structure as the plain decode kernel (one workgroup per sequence, KV
 // head and split; whole-row loads; K rearranged through a per-wave LDS tile;
@@ -15,8 +15,8 @@
 //     block_table[b][key0 / block_size] (block_size a multiple of 32, so a
 //     step never crosses a block).  The resource's size ends at the last
 //     valid row, so rows at or past the split end read as zero.
-//   - FP8 rows are converted to bf16 (exact: every E4M3 value is a bf16
-//     value) when K is staged in LDS and when the V fragments are built.  The
+//   - FP8 rows are converted to bf16 (exact: every E4M3 and every E5M2 value
+//     is a bf16 value) when K is staged in LDS and when the V fragments are built.  The
 //     per-KV-head scales never touch the elements: k_scale multiplies the
 //     score factor and v_scale the output.
 // Splits write (m, l, acc) like the plain kernel; decode_ex_merge combines
@@ -52,22 +52,24 @@ __device__ __forceinline__ typename ExVRaw<D, KV8>::T ex_load_v(__amdgpu_buffer_
     else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamLoad);
 }
 
-// Two E4M3 bytes (low or high half of a word) -> two bf16 in one word.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+// Two FP8 bytes (low or high half of a word) -> two bf16 in one word; KV is
+// the cache format: 1 = E4M3, 2 = E5M2.
+template <int KV, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    if constexpr (KV == 2) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+    else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // V piece as bf16 words (the plain kernel's VFragT layout).
-template <int D, bool KV8>
-__device__ __forceinline__ typename VFragT<D>::T ex_v_bf16(typename ExVRaw<D, KV8>::T x) {
-    if constexpr (!KV8) {
+template <int D, int KV>
+__device__ __forceinline__ typename VFragT<D>::T ex_v_bf16(typename ExVRaw<D, KV != 0>::T x) {
+    if constexpr (KV == 0) {
         return x;
     } else if constexpr (D == 128) {
-        return u32x4{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
-                     e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
+        return u32x4{fp8x2_to_bf16x2<KV, false>(x[0]), fp8x2_to_bf16x2<KV, true>(x[0]),
+                     fp8x2_to_bf16x2<KV, false>(x[1]), fp8x2_to_bf16x2<KV, true>(x[1])};
     } else {
-        return u32x2{e4m3x2_to_bf16x2<false>(x), e4m3x2_to_bf16x2<true>(x)};
+        return u32x2{fp8x2_to_bf16x2<KV, false>(x), fp8x2_to_bf16x2<KV, true>(x)};
     }
 }
 
@@ -95,8 +97,9 @@ __device__ __forceinline__ void ex_load_step(ExStepData<D, KV8>& st, __amdgpu_bu
 
 // K rows into the wave's LDS tile as bf16, in the plain kernel's swizzled
 // layout (row kl, 16-byte bf16 chunk c at kl*CPR + (c ^ (kl % CPR))).
-template <int D, bool KV8>
-__device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV8>& st, u32x4* kt, int lane) {
+template <int D, int KV>
+__device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV != 0>& st, u32x4* kt, int lane) {
+    constexpr bool KV8 = KV != 0;
     typedef ExShape<D, KV8> Sh;
     constexpr int CPR16 = DecodeShape<D>::CPR;  // bf16 chunks per row
 #pragma unroll
@@ -108,10 +111,10 @@ __device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV8>& st, u32x4* 
         } else {
             // 16 E4M3 values = head dims 16c .. 16c+15 = bf16 chunks 2c, 2c+1
             const u32x4 w = st.kR[i];
-            const u32x4 lo = u32x4{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
-                                   e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
-            const u32x4 hi = u32x4{e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
-                                   e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
+            const u32x4 lo = u32x4{fp8x2_to_bf16x2<KV, false>(w[0]), fp8x2_to_bf16x2<KV, true>(w[0]),
+                                   fp8x2_to_bf16x2<KV, false>(w[1]), fp8x2_to_bf16x2<KV, true>(w[1])};
+            const u32x4 hi = u32x4{fp8x2_to_bf16x2<KV, false>(w[2]), fp8x2_to_bf16x2<KV, true>(w[2]),
+                                   fp8x2_to_bf16x2<KV, false>(w[3]), fp8x2_to_bf16x2<KV, true>(w[3])};
             kt[kl * CPR16 + ((2 * c) ^ (kl % CPR16))] = lo;
             kt[kl * CPR16 + ((2 * c + 1) ^ (kl % CPR16))] = hi;
         }
@@ -120,8 +123,8 @@ __device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV8>& st, u32x4* 
 
 // Scores, masked online softmax and P*V of one step.  lo/hi: inclusive key
 // range of each lane's query row (per 16-row tile); end: split end.
-template <int D, int NT, bool KV8>
-__device__ __forceinline__ void ex_compute_step(const ExStepData<D, KV8>& st, const u32x4* kt,
+template <int D, int NT, int KV>
+__device__ __forceinline__ void ex_compute_step(const ExStepData<D, KV != 0>& st, const u32x4* kt,
                                                 int key0, int end, int lane, float c_log2,
                                                 const int (&lo)[NT], const int (&hi)[NT],
                                                 const bf16x8 (&qB)[NT][DecodeShape<D>::KI],
@@ -141,7 +144,7 @@ __device__ __forceinline__ void ex_compute_step(const ExStepData<D, KV8>& st, co
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vB[t][r] = ex_v_bf16<D, KV8>(st.vB[t][r]);
+        for (int r = 0; r < 4; ++r) vB[t][r] = ex_v_bf16<D, KV>(st.vB[t][r]);
     // element 4t+r of lane (col, grp): V[key0 + 16t + 4grp + r][EPL*col + e]
     u32x4 vT[Sh::EPL];
 #pragma unroll
@@ -223,7 +226,7 @@ __device__ __forceinline__ int ex_first_key(int n, int T, int window) {
 // NT = ceil(T * gsize / 16) tiles of 16 query rows; NWV waves per workgroup
 // take the split's 32-key steps in turn.
 // ---------------------------------------------------------------------------
-template <int D, int NT, bool KV8, int NWV>
+template <int D, int NT, int KV, int NWV>
 __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, const float* __restrict__ k_scale,
@@ -231,6 +234,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     int bs, int T, int Hq, int Hkv, int Lmax, int gsize, int S, int chunk, int window,
     float c_log2, uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml) {
+    constexpr bool KV8 = KV != 0;  // one-byte FP8 rows (KV: 1 = E4M3, 2 = E5M2)
     typedef DecodeShape<D> Sh;
     typedef ExShape<D, KV8> Ex;
     constexpr int KI = Sh::KI;
@@ -321,16 +325,16 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
         for (; key0 < end; key0 += stride) {
             ExStepData<D, KV8> nxt;
             if (key0 + stride < end) load(key0 + stride, nxt);
-            ex_stage_k<D, KV8>(cur, kt, lane);
-            ex_compute_step<D, NT, KV8>(cur, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
+            ex_stage_k<D, KV>(cur, kt, lane);
+            ex_compute_step<D, NT, KV>(cur, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
             cur = nxt;
         }
     } else {
         for (int key0 = kbeg + wave * kDecodeStep; key0 < end; key0 += stride) {
             ExStepData<D, KV8> st;
             load(key0, st);
-            ex_stage_k<D, KV8>(st, kt, lane);
-            ex_compute_step<D, NT, KV8>(st, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
+            ex_stage_k<D, KV>(st, kt, lane);
+            ex_compute_step<D, NT, KV>(st, kt, key0, end, lane, cs, lo, hi, qB, O, m_run, l_run);
         }
     }
 

@@ -125,7 +125,7 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
     gqa_status st = check_heads(a->Hq, a->Hkv, a->d);
     if (st != GQA_OK) return st;
     if (a->dtype != GQA_BF16) return GQA_ERR_DTYPE;
-    if (a->kv_dtype != GQA_BF16 && a->kv_dtype != GQA_FP8_E4M3) return GQA_ERR_DTYPE;
+    if (a->kv_dtype != GQA_BF16 && a->kv_dtype != GQA_FP8_E4M3 && a->kv_dtype != GQA_FP8_E5M2) return GQA_ERR_DTYPE;
     if ((int64_t)a->T * (a->Hq / a->Hkv) > kMaxGroup) return GQA_ERR_UNSUPPORTED;
     if (a->block_table) {
         if (a->block_size < 32 || a->block_size % 32 != 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
@@ -156,17 +156,17 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
     if ((int64_t)a->B * a->Hkv * splits > INT_MAX || rows > INT_MAX) return GQA_ERR_SHAPE;
     plan->splits = (int)splits;
     plan->chunk = (int)chunk;
-    plan->elt = a->kv_dtype == GQA_FP8_E4M3 ? 1 : 2;
+    plan->elt = a->kv_dtype == GQA_BF16 ? 2 : 1;
     plan->ws_bytes = splits > 1 ? (size_t)rows * splits * (a->d + 2) * sizeof(float) : 0;
     return GQA_OK;
 }
 
-// Waves per workgroup of the extended kernel: an E4M3 step moves half the
+// Waves per workgroup of the extended kernel: an FP8 step moves half the
 // bytes of a bf16 step, so twice the waves keep as many bytes in flight
 // (up to 32 query rows; more rows need more registers than 8 waves allow).
 template <bool KV8, int NT> constexpr int ex_waves() { return KV8 && NT <= 2 ? 8 : 4; }
 
-template <int D, bool KV8>
+template <int D, int KV>
 void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_args* a, const ExPlan& p,
                       float c, float* wa, float* wm) {
     dim3 block;
@@ -178,10 +178,10 @@ void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_arg
 #define GQA_EX_ARGS q, k, v, a->seqlens, a->k_scale, a->v_scale, a->block_table, a->max_blocks, \
                     a->block_size, a->T, a->Hq, a->Hkv, a->Lmax, gs, p.splits, p.chunk, a->window, c, o, wa, wm
     switch (nt) {
-        case 1: block = dim3(64 * ex_waves<KV8, 1>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 1, KV8, ex_waves<KV8, 1>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        case 2: block = dim3(64 * ex_waves<KV8, 2>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 2, KV8, ex_waves<KV8, 2>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        case 3: block = dim3(64 * ex_waves<KV8, 3>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 3, KV8, ex_waves<KV8, 3>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        default: block = dim3(64 * ex_waves<KV8, 4>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 4, KV8, ex_waves<KV8, 4>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 1: block = dim3(64 * ex_waves<KV != 0, 1>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 1, KV, ex_waves<KV != 0, 1>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 2: block = dim3(64 * ex_waves<KV != 0, 2>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 2, KV, ex_waves<KV != 0, 2>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 3: block = dim3(64 * ex_waves<KV != 0, 3>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 3, KV, ex_waves<KV != 0, 3>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        default: block = dim3(64 * ex_waves<KV != 0, 4>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 4, KV, ex_waves<KV != 0, 4>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
     }
 #undef GQA_EX_ARGS
 }
@@ -320,7 +320,8 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
     if (!a) return GQA_ERR_NULL;
     if (!a->q || !a->k_cache || !a->v_cache || !a->seqlens || !a->out) return GQA_ERR_NULL;
     if ((a->k_new == nullptr) != (a->v_new == nullptr)) return GQA_ERR_NULL;
-    if (a->kv_dtype == GQA_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return GQA_ERR_NULL;
+    const bool kv_fp8 = a->kv_dtype == GQA_FP8_E4M3 || a->kv_dtype == GQA_FP8_E5M2;
+    if (kv_fp8 && (!a->k_scale || !a->v_scale)) return GQA_ERR_NULL;
     if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->out))
         return GQA_ERR_ALIGN;
     if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return GQA_ERR_ALIGN;
@@ -338,7 +339,6 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
     const int64_t rows = (int64_t)a->B * a->T * a->Hq;
     float* ws_acc = plan.ws_bytes ? static_cast<float*>(a->workspace) : nullptr;
     float* ws_ml = plan.ws_bytes ? ws_acc + rows * S * a->d : nullptr;
-    const bool fp8 = a->kv_dtype == GQA_FP8_E4M3;
     (void)hipGetLastError();
     if (a->k_new) {
         const int rowb = a->d * plan.elt;
@@ -351,11 +351,13 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
     const float c = a->scale * gqa::kLog2e;
     dim3 grid((unsigned)((int64_t)a->B * a->Hkv * S));
     if (a->d == 128) {
-        if (fp8) launch_decode_ex<128, true>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else launch_decode_ex<128, false>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        if (a->kv_dtype == GQA_FP8_E4M3) launch_decode_ex<128, 1>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else if (a->kv_dtype == GQA_FP8_E5M2) launch_decode_ex<128, 2>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else launch_decode_ex<128, 0>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
     } else {
-        if (fp8) launch_decode_ex<64, true>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else launch_decode_ex<64, false>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        if (a->kv_dtype == GQA_FP8_E4M3) launch_decode_ex<64, 1>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else if (a->kv_dtype == GQA_FP8_E5M2) launch_decode_ex<64, 2>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+        else launch_decode_ex<64, 0>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
     }
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     if (S > 1) {

@@ -42,7 +42,8 @@ extern "C" {
 typedef enum {
     GQA_F32 = 0,
     GQA_BF16 = 1,
-    GQA_FP8_E4M3 = 2 /* OCP 8-bit float E4M3 (bias 7, no infinities); KV caches of gqa_decode_ex only */
+    GQA_FP8_E4M3 = 2, /* OCP 8-bit float E4M3 (bias 7, no infinities); KV caches of gqa_decode_ex only */
+    GQA_FP8_E5M2 = 3  /* OCP 8-bit float E5M2 (bias 15, IEEE-style infinities and NaNs); KV caches of gqa_decode_ex only */
 } gqa_dtype;
 
 typedef enum {
@@ -159,8 +160,8 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P
  * aligned where they hold rows):
  *   q        [B, T, Hq, d] bf16 (dtype must be GQA_BF16)
  *   out      [B, T, Hq, d] bf16
- *   k_cache, v_cache   the cache, element type kv_dtype (GQA_BF16 or
- *            GQA_FP8_E4M3): contiguous [B, Lmax, Hkv, d] when block_table is
+ *   k_cache, v_cache   the cache, element type kv_dtype (GQA_BF16,
+ *            GQA_FP8_E4M3 or GQA_FP8_E5M2): contiguous [B, Lmax, Hkv, d] when block_table is
  *            NULL; otherwise a pool [num_blocks, block_size, Hkv, d] and row j
  *            of sequence b is row j % block_size of block
  *            block_table[b * max_blocks + j / block_size].  Written when
@@ -170,8 +171,9 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P
  *   block_table  [B, max_blocks] int32 or NULL.  block_size must be a multiple
  *            of 32; Lmax must equal max_blocks * block_size.  Precondition:
  *            every entry used is in [0, num_blocks).
- *   k_scale, v_scale  [Hkv] fp32, GQA_FP8_E4M3 only: K row values are
- *            e4m3(byte) * k_scale[g], V likewise with v_scale[g].
+ *   k_scale, v_scale  [Hkv] fp32, the FP8 formats only (required there,
+ *            ignored for bf16): K row values are fp8(byte) * k_scale[g], V
+ *            likewise with v_scale[g], fp8() the value the format encodes.
  *   k_new, v_new  [B, T, Hkv, d] in kv_dtype, or both NULL.  When given they
  *            are first stored, byte for byte, at rows seqlens[b] - T + t.
  *   window   0 = every key; W > 0 = the last W keys of each token.

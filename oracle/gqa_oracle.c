@@ -369,9 +369,10 @@ int oracle_mqa_decode(const void *q, const void *k, const void *v, const int32_t
  *     pos = n - T + t and attends keys j <= pos: the causal rule of prefill
  *     ("从MHA到GQA", causal mask section) applied to the new tokens.
  *   - Sliding window W > 0: only keys j in [pos - W + 1, pos].
- *   - Cache rows stored as fp32 / bf16 (dtype 0 / 1, like q), or as OCP FP8
- *     E4M3 bytes (kv_fp8 = 1) whose value is decode(byte) * k_scale[g] for K
- *     and decode(byte) * v_scale[g] for V, one scale per KV head g.
+ *   - Cache rows stored as fp32 / bf16 (kv_fmt = 0: q's dtype), or as OCP
+ *     FP8 bytes, E4M3 (kv_fmt = 1) or E5M2 (kv_fmt = 2), whose value is
+ *     decode(byte) * k_scale[g] for K and decode(byte) * v_scale[g] for V,
+ *     one scale per KV head g.
  *   - Cache addressing: contiguous [B,Lmax,Hkv,d] (block_table == NULL), or
  *     paged: row j of sequence b is row j % bs of block
  *     block_table[b*max_blocks + j / bs] in a pool [nblocks,bs,Hkv,d].
@@ -397,6 +398,23 @@ double oracle_e4m3_value(unsigned byte)
     return sgn ? -v : v;
 }
 
+/* OCP FP8 E5M2: sign, 5 exponent bits with bias 15, 2 mantissa bits, laid
+ * out like the top byte of an IEEE half; exponent 0 is subnormal
+ * (m/4 * 2^-14); exponent 31 holds +-infinity (m = 0) and NaN (m != 0); the
+ * largest finite value is 1.75 * 2^15 = 57344. */
+double oracle_e5m2_value(unsigned byte)
+{
+    const int sgn = (byte >> 7) & 1, e = (byte >> 2) & 31, m = byte & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m / 4.0, -14);
+    else
+        v = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return sgn ? -v : v;
+}
+
 /* Element offset of cached row j of sequence b, KV head g. */
 static int64_t orc_row_ex(int64_t b, int64_t j, int64_t g, int64_t Hkv, int64_t d, int64_t Lmax,
                           const int32_t *block_table, int64_t max_blocks, int64_t bs)
@@ -407,16 +425,18 @@ static int64_t orc_row_ex(int64_t b, int64_t j, int64_t g, int64_t Hkv, int64_t 
     return ((blk * bs + j % bs) * Hkv + g) * d;
 }
 
-static double orc_kv_elem(const void *base, int64_t idx, int dtype, int kv_fp8, double scale)
+static double orc_kv_elem(const void *base, int64_t idx, int dtype, int kv_fmt, double scale)
 {
-    if (kv_fp8)
+    if (kv_fmt == 1)
         return oracle_e4m3_value(((const uint8_t *)base)[idx]) * scale;
+    if (kv_fmt == 2)
+        return oracle_e5m2_value(((const uint8_t *)base)[idx]) * scale;
     return orc_elem(base, idx, dtype);
 }
 
 int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t *seqlens,
                      int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64_t Lmax,
-                     double scale, int dtype, int kv_fp8, const float *k_scale,
+                     double scale, int dtype, int kv_fmt, const float *k_scale,
                      const float *v_scale, const int32_t *block_table, int64_t max_blocks,
                      int64_t bs, int64_t window, const int64_t *rows, int64_t nrows, double *out)
 {
@@ -425,7 +445,7 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
         return rc;
     if (T <= 0 || Lmax < 0 || window < 0)
         return -1;
-    if (kv_fp8 && (!k_scale || !v_scale))
+    if (kv_fmt < 0 || kv_fmt > 2 || (kv_fmt && (!k_scale || !v_scale)))
         return -1;
     if (block_table && (bs <= 0 || max_blocks <= 0 || Lmax > max_blocks * bs))
         return -1;
@@ -458,8 +478,8 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
                 const int64_t pos = seqlens[b] - T + t;
                 const int64_t lo = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
                 const int64_t n = pos - lo + 1; /* keys lo .. pos */
-                const double ks = kv_fp8 ? (double)k_scale[g] : 1.0;
-                const double vs = kv_fp8 ? (double)v_scale[g] : 1.0;
+                const double ks = kv_fmt ? (double)k_scale[g] : 1.0;
+                const double vs = kv_fmt ? (double)v_scale[g] : 1.0;
                 const int64_t qrow = (bt * Hq + h) * d;
                 double *o = out + i * d;
                 /* scores, j ascending over the visible keys */
@@ -467,7 +487,7 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
                     const int64_t kr = orc_row_ex(b, lo + jj, g, Hkv, d, Lmax, block_table, max_blocks, bs);
                     double dot = 0.0;
                     for (int64_t c = 0; c < d; ++c)
-                        dot += orc_elem(q, qrow + c, dtype) * orc_kv_elem(k, kr + c, dtype, kv_fp8, ks);
+                        dot += orc_elem(q, qrow + c, dtype) * orc_kv_elem(k, kr + c, dtype, kv_fmt, ks);
                     w[jj] = dot * scale;
                 }
                 double m = w[0];
@@ -484,7 +504,7 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
                 for (int64_t jj = 0; jj < n; ++jj) {
                     const int64_t vr = orc_row_ex(b, lo + jj, g, Hkv, d, Lmax, block_table, max_blocks, bs);
                     for (int64_t c = 0; c < d; ++c)
-                        acc[c] += w[jj] * orc_kv_elem(v, vr + c, dtype, kv_fp8, vs);
+                        acc[c] += w[jj] * orc_kv_elem(v, vr + c, dtype, kv_fmt, vs);
                 }
                 for (int64_t c = 0; c < d; ++c)
                     o[c] = acc[c] / z;
@@ -501,7 +521,7 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
  * new K/V rows of sequence b, k_new/v_new [B,T,Hkv,d], are stored at cache
  * rows seqlens[b] - T + t (seqlens counts them already), contiguous or paged
  * as in oracle_decode_ex.  elt = bytes per stored element (4 fp32, 2 bf16,
- * 1 e4m3); the rows are copied byte for byte.
+ * 1 FP8); the rows are copied byte for byte.
  */
 int oracle_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                   const int32_t *seqlens, int64_t B, int64_t T, int64_t Hkv, int64_t d,

@@ -56,6 +56,8 @@ def _bind(lib):
     lib.oracle_append.restype = ci
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint]
     lib.oracle_e4m3_value.restype = dbl
+    lib.oracle_e5m2_value.argtypes = [ctypes.c_uint]
+    lib.oracle_e5m2_value.restype = dbl
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
     return lib
@@ -214,13 +216,22 @@ def e4m3_value(byte: int) -> float:
     return _load().oracle_e4m3_value(int(byte) & 0xFF)
 
 
+def e5m2_value(byte: int) -> float:
+    """Value of one OCP FP8 E5M2 byte (+-inf for S.11111.00, NaN for S.11111.mm, mm != 0)."""
+    return _load().oracle_e5m2_value(int(byte) & 0xFF)
+
+
+_KV_FORMATS = {"e4m3": 1, "e5m2": 2}
+
+
 def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_table=None,
-              block_size=0, window=0, rows=None) -> np.ndarray:
+              block_size=0, window=0, rows=None, kv_format="e4m3") -> np.ndarray:
     """Extended GQA decode.  q [B,T,Hq,d] (fp32 or bf16 bits).
 
     k, v: contiguous [B,Lmax,Hkv,d] or, with ``block_table`` [B,max_blocks],
-    a paged pool [nblocks,block_size,Hkv,d]; stored in q's dtype, or as E4M3
-    bytes (uint8) scaled per KV head by ``k_scale``/``v_scale`` [Hkv].
+    a paged pool [nblocks,block_size,Hkv,d]; stored in q's dtype, or as FP8
+    bytes (uint8) in ``kv_format`` ("e4m3" or "e5m2") scaled per KV head by
+    ``k_scale``/``v_scale`` [Hkv].
     seqlens [B] counts the T new tokens; token t sits at seqlens[b]-T+t.
     window > 0 keeps the last ``window`` keys of every token.  Returns
     [B,T,Hq,d] float64, or [len(rows),d] for flat ((b*T+t)*Hq+h) rows.
@@ -228,8 +239,8 @@ def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_tabl
     q, k, v = _c(q), _c(k), _c(v)
     dt = _dtype_code(q)
     B, T, Hq, d = q.shape
-    fp8 = k.dtype == np.uint8
-    if fp8:
+    fmt = _KV_FORMATS[kv_format] if k.dtype == np.uint8 else 0
+    if fmt:
         assert v.dtype == np.uint8 and k_scale is not None and v_scale is not None
     else:
         assert _dtype_code(k) == dt and _dtype_code(v) == dt
@@ -256,7 +267,7 @@ def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_tabl
         out = np.empty((r.size, d), np.float64)
         nrows = r.size
     rc = _load().oracle_decode_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
-                                  B, T, Hq, Hkv, d, Lmax, float(scale), dt, 1 if fp8 else 0,
+                                  B, T, Hq, Hkv, d, Lmax, float(scale), dt, fmt,
                                   _ptr(ks), _ptr(vs), _ptr(bt), maxb, bs, int(window), _ptr(r),
                                   nrows, out.ctypes.data)
     if rc:

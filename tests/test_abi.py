@@ -182,6 +182,9 @@ def _ex_args(**kw):
     (dict(seqlens=None), Status.ERR_NULL),
     (dict(k_new=FAKE), Status.ERR_NULL),                         # v_new missing
     (dict(kv_dtype=gqa.FP8_E4M3), Status.ERR_NULL),              # scales missing
+    (dict(kv_dtype=gqa.FP8_E5M2), Status.ERR_NULL),              # scales missing
+    (dict(kv_dtype=gqa.FP8_E5M2, k_scale=FAKE, v_scale=FAKE, T=17), Status.ERR_UNSUPPORTED),
+    (dict(kv_dtype=4, k_scale=FAKE, v_scale=FAKE), Status.ERR_DTYPE),
     (dict(q=FAKE + 2), Status.ERR_ALIGN),
     (dict(k_new=FAKE + 8, v_new=FAKE), Status.ERR_ALIGN),
     (dict(T=0), Status.ERR_SHAPE),

@@ -1,7 +1,7 @@
 """GPU parity of gqa_decode_ex against the fp64 CPU oracle (needs an MI355X).
 
 Covers several new tokens per sequence, the append of their K/V rows, FP8
-(E4M3) caches with per-KV-head scales, paged caches and sliding windows, alone
+(E4M3 and E5M2) caches with per-KV-head scales, paged caches and sliding windows, alone
 and combined, with forced and automatic splits.  Tolerance (bf16 q and out,
 fp32 accumulation): |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise.
 Cache rows past each length, pool blocks no sequence uses and the rows of the
@@ -33,9 +33,10 @@ def run_ex(c, append=True, num_splits=0):
     v = _dev_cache(c.v_pre if append else c.v)
     sl = torch.from_numpy(c.seqlens).cuda()
     kw = {}
-    if c.kv == "fp8":
+    if c.kv_format:
         kw["k_scale"] = torch.from_numpy(c.k_scale).cuda()
         kw["v_scale"] = torch.from_numpy(c.v_scale).cuda()
+        kw["kv_format"] = c.kv_format
     if c.block_table is not None:
         kw["block_table"] = torch.from_numpy(c.block_table).cuda()
         kw["block_size"] = c.block_size
@@ -50,7 +51,7 @@ def run_ex(c, append=True, num_splits=0):
 def oracle_ex(c, rows=None):
     return orc.decode_ex(c.q, c.k, c.v, c.seqlens, c.scale, k_scale=c.k_scale, v_scale=c.v_scale,
                          block_table=c.block_table, block_size=c.block_size, window=c.window,
-                         rows=rows)
+                         rows=rows, kv_format=c.kv_format or "e4m3")
 
 
 def check(c, got, ref):
@@ -77,7 +78,7 @@ def test_tokens_and_groups(d, T, Hq, Hkv):
     check(c, from_dev(out), oracle_ex(c))
 
 
-@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("kv", ["same", "fp8", "e5m2"])
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
 def test_splits(kv, splits):
     c = case(kv=kv, T=3, seqlens=(256, 200, 33), seed=42)
@@ -85,15 +86,60 @@ def test_splits(kv, splits):
     check(c, from_dev(out), oracle_ex(c))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "e5m2"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("T", [1, 4])
-def test_fp8_cache(d, T):
-    c = case(kv="fp8", d=d, T=T, seed=43)
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_fp8_cache(kv, d, T):
+    c = case(kv=kv, d=d, T=T, Hq=32 if T == 8 else 16, seqlens=(256, 97, max(T, 5)), seed=43)
     out, _, _ = run_ex(c)
     check(c, from_dev(out), oracle_ex(c))
 
 
-@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_every_finite_code_converts_exactly(fmt):
+    """One visible key: every query head returns its V row, v_scale 1.  The V
+    row holds every finite code of the format (subnormals and the extremes
+    included), and each is a bf16 value, so the output must equal it bit for
+    bit."""
+    kind = "fp8" if fmt == "e4m3" else "e5m2"
+    c = case(B=1, T=1, Hq=8, Hkv=2, d=128, Lmax=32, seqlens=(1,), kv=kind, seed=52)
+    val = orc.e4m3_value if fmt == "e4m3" else orc.e5m2_value
+    finite = [x for x in range(256) if np.isfinite(val(x))]
+    codes = np.zeros(256, np.uint8)
+    codes[:len(finite)] = finite
+    c.v[0, 0] = codes.reshape(2, 128)
+    c.v_scale = np.ones(2, np.float32)
+    out, _, _ = run_ex(c, append=False)
+    want = np.array([val(int(x)) for x in codes]).reshape(2, 128)
+    got = from_dev(out)[0, 0]
+    for h in range(8):
+        assert np.array_equal(got[h], want[h // 4]), h
+    assert np.array_equal(got, oracle_ex(c)[0, 0])
+
+
+def test_fp8_dtypes_name_their_format():
+    """A float8_e5m2 (or float8_e4m3fn) cache needs no kv_format; a uint8 one
+    is read as the kv_format it is given."""
+    c = case(kv="e5m2", T=2, seed=53)
+    ref = oracle_ex(c)
+    sl = torch.from_numpy(c.seqlens).cuda()
+    ks, vs = torch.from_numpy(c.k_scale).cuda(), torch.from_numpy(c.v_scale).cuda()
+    k = _dev_cache(c.k).view(torch.float8_e5m2)
+    v = _dev_cache(c.v).view(torch.float8_e5m2)
+    out = gqa.decode_ex(to_dev(c.q), k, v, sl, scale=c.scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    check(c, from_dev(out), ref)
+    with pytest.raises(TypeError):
+        gqa.decode_ex(to_dev(c.q), k, v, sl, scale=c.scale, k_scale=ks, v_scale=vs,
+                      kv_format="e4m3")
+    # the same bytes read as E4M3 are other numbers
+    as_e4m3 = gqa.decode_ex(to_dev(c.q), k.view(torch.uint8), v.view(torch.uint8), sl,
+                            scale=c.scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert not np.array_equal(from_dev(as_e4m3), from_dev(out))
+
+
+@pytest.mark.parametrize("kv", ["same", "fp8", "e5m2"])
 @pytest.mark.parametrize("block_size", [32, 64, 128])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_paged(kv, block_size, splits):
@@ -110,15 +156,17 @@ def test_window(window, splits):
     check(c, from_dev(out), oracle_ex(c))
 
 
-def test_everything_together():
-    c = case(B=4, T=4, Hq=32, Hkv=4, kv="fp8", paged=True, block_size=32, window=45,
+@pytest.mark.parametrize("kv", ["fp8", "e5m2"])
+def test_everything_together(kv):
+    c = case(B=4, T=4, Hq=32, Hkv=4, kv=kv, paged=True, block_size=32, window=45,
              seqlens=(256, 161, 64, 4), seed=46)
     for splits in (0, 1, 5):
         out, _, _ = run_ex(c, num_splits=splits)
         check(c, from_dev(out), oracle_ex(c))
 
 
-@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", False), ("fp8", True)])
+@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", False), ("fp8", True),
+                                      ("e5m2", False), ("e5m2", True)])
 def test_append_writes_cache_rows_exactly(kv, paged):
     c = case(kv=kv, paged=paged, T=4, seed=47)
     out, k, v = run_ex(c, append=True)
@@ -148,11 +196,12 @@ def test_single_token_matches_plain_decode():
     assert ok, err
 
 
-def test_fp8_70b_layer_sampled():
+@pytest.mark.parametrize("kv", ["fp8", "e5m2"])
+def test_fp8_70b_layer_sampled(kv):
     """The 70B-class layer shape with an FP8 cache and 4 new tokens per sequence,
     sampled rows against the oracle."""
-    c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096] * 32, "bf16", seed=50, kv="fp8",
-                          invalid="zero", name="ex_fp8_B32_T4_Hq64_Hkv8_d128_L4096")
+    c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096] * 32, "bf16", seed=50, kv=kv,
+                          invalid="zero", name="ex_%s_B32_T4_Hq64_Hkv8_d128_L4096" % kv)
     out, _, _ = run_ex(c)
     rng = np.random.default_rng(7)
     rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))

@@ -1,6 +1,6 @@
 """Pins of the extended decode oracle (several new tokens, append, sliding
-window, paged cache, FP8 E4M3 cache) against things other than itself: the
-E4M3 definition and torch's float8 cast, the separately written decode and
+window, paged cache, FP8 E4M3 and E5M2 caches) against things other than
+itself: the two formats' definitions and torch's float8 casts, the separately written decode and
 prefill oracles, cache slices, closed forms, and the pure-Python brute force.
 """
 import os
@@ -12,47 +12,67 @@ import gqa_inputs as gi
 from oracle import brute, reference as orc
 from tests.helpers import widen
 
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "e4m3_values.txt")
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def _golden_e4m3():
+def _golden_fp8(fname):
     rows = []
-    for line in open(GOLDEN):
+    for line in open(os.path.join(GOLDEN_DIR, fname)):
         line = line.split("#")[0].strip()
         if not line:
             continue
         code, val = line.split()[:2]
-        if val == "nan":
-            rows.append((int(code, 16), float("nan")))
+        if val in ("nan", "inf", "-inf"):
+            rows.append((int(code, 16), float(val)))
         else:
             mant, exp = val.split("*2^")
             rows.append((int(code, 16), float(mant) * 2.0 ** int(exp) if mant != "-0" else -0.0))
     return rows
 
 
-def test_e4m3_golden_values():
-    for code, val in _golden_e4m3():
-        got = orc.e4m3_value(code)
+@pytest.mark.parametrize("fname,fn", [("e4m3_values.txt", orc.e4m3_value),
+                                      ("e5m2_values.txt", orc.e5m2_value)])
+def test_fp8_golden_values(fname, fn):
+    for code, val in _golden_fp8(fname):
+        got = fn(code)
         if np.isnan(val):
             assert np.isnan(got), hex(code)
         else:
             assert got == val and np.signbit(got) == np.signbit(val), hex(code)
 
 
-def test_e4m3_matches_torch_cast_all_codes():
+def _torch_fp8(fmt):
     torch = pytest.importorskip("torch")
+    return torch, {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+
+
+@pytest.mark.parametrize("fmt,fn", [("e4m3", orc.e4m3_value), ("e5m2", orc.e5m2_value)])
+def test_fp8_matches_torch_cast_all_codes(fmt, fn):
+    torch, tdt = _torch_fp8(fmt)
     codes = np.arange(256, dtype=np.uint8)
-    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    got = np.array([orc.e4m3_value(c) for c in codes])
+    ref = torch.from_numpy(codes).view(tdt).to(torch.float64).numpy()
+    got = np.array([fn(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e5m2_is_the_top_byte_of_a_half():
+    """E5M2 shares binary16's sign and exponent fields: code c is the half
+    with bits c << 8, for every one of the 256 codes."""
+    codes = np.arange(256, dtype=np.uint16)
+    ref = (codes << 8).astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([orc.e5m2_value(int(c)) for c in codes])
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert np.array_equal(got[ok], ref[ok])
 
 
-def _e4m3_widen(codes, scale_per_head):
+def _fp8_widen(codes, scale_per_head, fmt="e4m3"):
     """FP8 rows [..., Hkv, d] -> float64 values * per-head scale, via torch's cast."""
-    import torch
-    vals = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    torch, tdt = _torch_fp8(fmt)
+    vals = torch.from_numpy(np.ascontiguousarray(codes)).view(tdt).to(torch.float64).numpy()
     return vals * np.asarray(scale_per_head, np.float64)[:, None]
 
 
@@ -105,40 +125,45 @@ def test_window_one_returns_own_value_row():
                 assert np.array_equal(got[b, t, h], widen(c.v[b, pos, h // 2]))
 
 
-@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("kv", ["same", "fp8", "e5m2"])
 def test_paged_equals_contiguous(kv):
     args = dict(B=3, T=2, Hq=8, Hkv=2, d=16, Lmax=64, seqlens=[64, 33, 2], dtype="bf16", seed=26,
                 kv=kv, block_size=16, window=0)
     flat = gi.decode_ex_case(**args)
     paged = gi.decode_ex_case(**args, paged=True)
+    fmt = flat.kv_format or "e4m3"
     a = orc.decode_ex(flat.q, flat.k, flat.v, flat.seqlens, flat.scale, k_scale=flat.k_scale,
-                      v_scale=flat.v_scale)
+                      v_scale=flat.v_scale, kv_format=fmt)
     b = orc.decode_ex(paged.q, paged.k, paged.v, paged.seqlens, paged.scale, k_scale=paged.k_scale,
                       v_scale=paged.v_scale, block_table=paged.block_table,
-                      block_size=paged.block_size)
+                      block_size=paged.block_size, kv_format=fmt)
     assert np.array_equal(a, b)
 
 
-def test_fp8_with_power_of_two_scales_equals_fp32_rows():
-    c = gi.decode_ex_case(2, 2, 8, 2, 32, 24, [24, 10], "f32", seed=27, kv="fp8")
+@pytest.mark.parametrize("kv", ["fp8", "e5m2"])
+def test_fp8_with_power_of_two_scales_equals_fp32_rows(kv):
+    c = gi.decode_ex_case(2, 2, 8, 2, 32, 24, [24, 10], "f32", seed=27, kv=kv)
     ks = np.array([0.25, 2.0], np.float32)
     vs = np.array([0.5, 0.125], np.float32)
-    got = orc.decode_ex(c.q, c.k, c.v, c.seqlens, c.scale, k_scale=ks, v_scale=vs)
-    k32 = _e4m3_widen(c.k, ks).astype(np.float32)   # exact: 4-bit significands times 2^k
-    v32 = _e4m3_widen(c.v, vs).astype(np.float32)
+    got = orc.decode_ex(c.q, c.k, c.v, c.seqlens, c.scale, k_scale=ks, v_scale=vs,
+                        kv_format=c.kv_format)
+    k32 = _fp8_widen(c.k, ks, c.kv_format).astype(np.float32)   # exact: short significands times 2^k
+    v32 = _fp8_widen(c.v, vs, c.kv_format).astype(np.float32)
     ref = orc.decode_ex(c.q, k32, v32, c.seqlens, c.scale)
     assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("kv,paged,window", [("same", False, 0), ("same", True, 5),
-                                             ("fp8", False, 4), ("fp8", True, 0)])
+                                             ("fp8", False, 4), ("fp8", True, 0),
+                                             ("e5m2", False, 3), ("e5m2", True, 0)])
 def test_matches_brute_force(kv, paged, window):
     c = gi.decode_ex_case(2, 3, 4, 2, 8, 12, [12, 5], "bf16", seed=28, kv=kv, paged=paged,
                           block_size=4, window=window)
     got = orc.decode_ex(c.q, c.k, c.v, c.seqlens, c.scale, k_scale=c.k_scale, v_scale=c.v_scale,
-                        block_table=c.block_table, block_size=c.block_size, window=window)
-    if kv == "fp8":
-        kw, vw = _e4m3_widen(c.k, c.k_scale), _e4m3_widen(c.v, c.v_scale)
+                        block_table=c.block_table, block_size=c.block_size, window=window,
+                        kv_format=c.kv_format or "e4m3")
+    if kv != "same":
+        kw, vw = _fp8_widen(c.k, c.k_scale, c.kv_format), _fp8_widen(c.v, c.v_scale, c.kv_format)
     else:
         kw, vw = widen(c.k), widen(c.v)
     ref = brute.decode_ex(widen(c.q).tolist(), kw.tolist(), vw.tolist(), c.seqlens.tolist(),
@@ -148,7 +173,8 @@ def test_matches_brute_force(kv, paged, window):
     assert np.allclose(got, np.array(ref), rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", True)])
+@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", True),
+                                      ("e5m2", False)])
 def test_append_stores_rows_exactly(kv, paged):
     c = gi.decode_ex_case(3, 4, 8, 2, 16, 32, [32, 9, 4], "bf16", seed=29, kv=kv, paged=paged,
                           block_size=8)

@@ -2,11 +2,14 @@
 
 Each mutant is a textual edit of ``oracle/gqa_oracle.c`` compiled into a
 temporary library; the pins below (brute force, closed forms, special cases)
-must reject every one.  The shipped oracle must pass the same pins.
+must reject every one.  The shipped oracle must pass the same pins.  Each
+mutant runs in a child interpreter: a mutant that indexes out of bounds may
+crash, and a crash counts as a failed pin.
 """
 import math
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -40,8 +43,14 @@ MUTANTS = {
                              "block_table[b * max_blocks + j % bs];"),
     "ex_e4m3_exponent_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
                               "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
-    "ex_v_scale_from_k": ("const double vs = kv_fp8 ? (double)v_scale[g] : 1.0;",
-                          "const double vs = kv_fp8 ? (double)k_scale[g] : 1.0;"),
+    "ex_v_scale_from_k": ("const double vs = kv_fmt ? (double)v_scale[g] : 1.0;",
+                          "const double vs = kv_fmt ? (double)k_scale[g] : 1.0;"),
+    "ex_e5m2_exponent_bias": ("v = ldexp(1.0 + (double)m / 4.0, e - 15);",
+                              "v = ldexp(1.0 + (double)m / 4.0, e - 16);"),
+    "ex_e5m2_mantissa_width": ("v = ldexp(1.0 + (double)m / 4.0, e - 15);",
+                               "v = ldexp(1.0 + (double)m / 8.0, e - 15);"),
+    "ex_e5m2_read_as_e4m3": ("if (kv_fmt == 2)\n        return oracle_e5m2_value",
+                             "if (kv_fmt == 2)\n        return oracle_e4m3_value"),
     "ex_append_row_off_by_one": ("const int64_t j = seqlens[b] - T + t;",
                                  "const int64_t j = seqlens[b] - T + t - 1;"),
     "query_row_of_wrong_head": ("orc_attend(q, (b * Hq + h) * d, k, v, ((b * Lmax) * Hkv + g) * d,\n",
@@ -100,6 +109,23 @@ def _pins():
             failed.append("brute_decode_ex")
     except orc.OracleError:
         failed.append("brute_decode_ex_error")
+    # E5M2 rows widened through binary16 (an E5M2 code is the top byte of a half)
+    e5 = gi.decode_ex_case(2, 2, 4, 2, 8, 10, [10, 5], "bf16", seed=34, kv="e5m2", window=3)
+    try:
+        got = orc.decode_ex(e5.q, e5.k, e5.v, e5.seqlens, e5.scale, k_scale=e5.k_scale,
+                            v_scale=e5.v_scale, window=3, kv_format="e5m2")
+
+        def w5(codes, sc):
+            half = (np.ascontiguousarray(codes).astype(np.uint16) << 8).view(np.float16)
+            return half.astype(np.float64) * np.asarray(sc, np.float64)[:, None]
+
+        ref = brute.decode_ex(widen(e5.q).tolist(), w5(e5.k, e5.k_scale).tolist(),
+                              w5(e5.v, e5.v_scale).tolist(), e5.seqlens.tolist(), e5.scale,
+                              window=3)
+        if not np.allclose(got, np.array(ref), rtol=1e-12, atol=1e-12):
+            failed.append("brute_decode_ex_e5m2")
+    except orc.OracleError:
+        failed.append("brute_decode_ex_e5m2_error")
     pf = gi.prefill_case(1, 9, 4, 2, 8, "bf16", seed=32)
     try:
         rows = orc.decode_ex(np.ascontiguousarray(pf.q[:, 6:]), pf.k, pf.v, np.array([9], np.int32),
@@ -146,11 +172,12 @@ def test_mutant_is_caught(name, src_text, tmp_path):
     lib = tmp_path / "libmutant.so"
     subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
                     "-o", str(lib), str(csrc), "-lm"], check=True)
-    prev = orc.swap_library(str(lib))
-    try:
-        failed = _pins()
-    finally:
-        orc.swap_library(None)
-        if prev is not None:
-            orc._lib = prev
-    assert failed, "mutant %s passed every pin" % name
+    child = ("import sys; from oracle import reference as orc; import tests.test_oracle_mutants as m; "
+             "orc.swap_library(sys.argv[1]); f = m._pins(); print(f); sys.exit(3 if f else 0)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-c", child, str(lib)], cwd=root, env=env,
+                       capture_output=True, text=True, timeout=300)
+    # 3: some pin failed; negative: killed by a signal (a crash is a failed pin)
+    assert r.returncode == 3 or r.returncode < 0, \
+        "mutant %s passed every pin (rc %d): %s %s" % (name, r.returncode, r.stdout, r.stderr[-400:])
