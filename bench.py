@@ -38,7 +38,8 @@ PREFILL_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/pr
 EXT_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/decode.hpp",
                "gqa_kv_cache_amd/csrc/decode_ex.hpp", "gqa_kv_cache_amd/csrc/gqa_api.hip")
 DECODE_PMC = "profiles/decode_bf16_B32_Hq64_Hkv8_d128_L4096.pmc.txt"
-EXT_FP8_PMC = "profiles/decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096.pmc.txt"
+EXT_FP8_PMC = {"e4m3": "profiles/decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096.pmc.txt",
+               "e5m2": "profiles/decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096.pmc.txt"}
 PREFILL_PMC = "profiles/prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal.pmc.txt"
 
 
@@ -365,8 +366,8 @@ def main():
             a.update(extra)
             c = gi.decode_ex_case(seed=60, name=name, **a)
             r = bench_decode_ex(c, max(20, args.steps // 2), args.warmup, torch, gqa)
-            if c.kv == "fp8":
-                r["traffic"] = pmc_traffic(EXT_FP8_PMC, EXT_SOURCES)
+            if c.kv_format:
+                r["traffic"] = pmc_traffic(EXT_FP8_PMC[c.kv_format], EXT_SOURCES)
             ext.append(r)
             del c
         line["extended"] = ext
