@@ -558,9 +558,103 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
 
 // ---------------------------------------------------------------------------
 // Merge of the split partials: M = max_s m_s, out = sum_s 2^(m_s-M) acc_s /
-// sum_s 2^(m_s-M) l_s over the non-empty splits s < ceil(seqlens[b]/chunk).
-// One 64-lane workgroup per (b, h) row.
+// sum_s 2^(m_s-M) l_s over the splits s in [s0, se) that hold keys of the
+// row (the plain decode: s0 = 0, se = ceil(seqlens[b]/chunk)).  One 64-lane
+// wave per row.  Lane i holds the (m, l) of split g0 + i of the current group
+// of 64 splits; every lane holds its D/64 columns of each split.  The row's
+// length, the first group's (m, l) pairs and the first 16 splits' columns
+// are all requested before the split range is known, so a row of up to 16
+// splits waits on memory once instead of once per split.  Slots outside the
+// range are never used (a select, not a multiply by 0, so stale workspace
+// contents cannot leak in).
 // ---------------------------------------------------------------------------
+constexpr int kMergeChunk = 16;  // splits whose columns are requested at once
+
+template <int D, typename Range>
+__device__ __forceinline__ float merge_split_row(const float* __restrict__ ws_acc,
+                                                 const float* __restrict__ ws_ml, int n,
+                                                 int64_t row, int S, Range range,
+                                                 float (&acc)[D / 64]) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x;
+    const float* arow = ws_acc + row * S * D + lane * PER;
+    const float* mrow = ws_ml + row * S * 2;
+    float m0 = kNegInf, l0 = 0.f;
+    if (lane < S) {
+        const float2 v = *reinterpret_cast<const float2*>(mrow + 2 * lane);
+        m0 = v.x;
+        l0 = v.y;
+    }
+    float a[kMergeChunk][PER];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+        if (i < S) {
+            if constexpr (PER == 2) {
+                const float2 v = *reinterpret_cast<const float2*>(arow + i * D);
+                a[i][0] = v.x;
+                a[i][PER - 1] = v.y;
+            } else {
+                a[i][0] = arow[i * D];
+            }
+        }
+    }
+    int s0, se;
+    range(n, s0, se);
+    // M over every split in range (further groups only when S > 64)
+    float M = (lane >= s0 && lane < se && m0 != kNegInf) ? m0 : kNegInf;
+    for (int g0 = 64; g0 < se; g0 += 64) {
+        const int sl = g0 + lane;
+        if (sl >= s0 && sl < se) {
+            const float m = mrow[2 * sl];
+            if (m != kNegInf) M = fmaxf(M, m);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+    float L = 0.f;
+    for (int g0 = 0; g0 < se; g0 += 64) {
+        float m = m0, l = l0;
+        const int sl = g0 + lane;
+        if (g0 > 0) {
+            m = kNegInf;
+            l = 0.f;
+            if (sl < se) {
+                m = mrow[2 * sl];
+                l = mrow[2 * sl + 1];
+            }
+        }
+        const bool mine = sl >= s0 && sl < se && m != kNegInf;
+        const float f = mine ? fast_exp2(m - M) : 0.f;
+        if (mine) L += f * l;
+        const int gend = min(se, g0 + 64);
+        for (int base = g0; base < gend; base += kMergeChunk) {
+            if (base > 0) {
+#pragma unroll
+                for (int i = 0; i < kMergeChunk; ++i) {
+                    if (base + i < gend) {
+#pragma unroll
+                        for (int p = 0; p < PER; ++p) a[i][p] = arow[(base + i) * D + p];
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kMergeChunk; ++i) {
+                const int s = base + i;
+                if (s >= s0 && s < gend) {
+                    const float fs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), s - g0));
+#pragma unroll
+                    for (int p = 0; p < PER; ++p) acc[p] += fs * a[i][p];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    return L;
+}
+
 template <int D, bool BF16OUT>
 __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws_acc,
                                                    const float* __restrict__ ws_ml,
@@ -568,23 +662,13 @@ __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws_
                                                    int S, int chunk, void* __restrict__ out) {
     constexpr int PER = D / 64;
     const int64_t row = blockIdx.x;
-    const int b = (int)(row / Hq);
-    const int n = seqlens[b];
-    const int se = min(S, (n + chunk - 1) / chunk);
+    const int n = seqlens[row / Hq];
+    float acc[PER];
+    const float L = merge_split_row<D>(ws_acc, ws_ml, n, row, S, [&](int len, int& s0, int& se) {
+        s0 = 0;
+        se = min(S, (len + chunk - 1) / chunk);
+    }, acc);
     const int c0 = threadIdx.x * PER;
-    const float* ml = ws_ml + row * S * 2;
-    float M = kNegInf;
-    for (int s = 0; s < se; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f, acc[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-    for (int s = 0; s < se; ++s) {
-        const float f = fast_exp2(ml[2 * s] - M);
-        L += f * ml[2 * s + 1];
-        const float* a = ws_acc + (row * S + s) * D + c0;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] += f * a[p];
-    }
     float o[PER];
 #pragma unroll
     for (int p = 0; p < PER; ++p) o[p] = L > 0.f ? acc[p] / L : 0.f;

@@ -418,24 +418,13 @@ __global__ __launch_bounds__(64) void decode_ex_merge(const float* __restrict__ 
                                                       uint16_t* __restrict__ out) {
     constexpr int PER = D / 64;
     const int64_t row = blockIdx.x;
-    const int b = (int)(row / ((int64_t)T * Hq));
-    const int n = seqlens[b];
-    const int s0 = ex_first_key(n, T, window) / chunk;
-    const int se = min(S, (n + chunk - 1) / chunk);
+    const int n = seqlens[row / ((int64_t)T * Hq)];
+    float acc[PER];
+    const float L = merge_split_row<D>(ws_acc, ws_ml, n, row, S, [&](int len, int& s0, int& se) {
+        s0 = ex_first_key(len, T, window) / chunk;
+        se = min(S, (len + chunk - 1) / chunk);
+    }, acc);
     const int c0 = threadIdx.x * PER;
-    const float* ml = ws_ml + row * S * 2;
-    float M = kNegInf;
-    for (int s = s0; s < se; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f, acc[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-    for (int s = s0; s < se; ++s) {
-        const float f = ml[2 * s] == kNegInf ? 0.f : fast_exp2(ml[2 * s] - M);
-        L += f * ml[2 * s + 1];
-        const float* a = ws_acc + (row * S + s) * D + c0;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] += f * a[p];
-    }
     uint16_t* dst = out + row * D + c0;
     if (PER == 2)
         *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2_rne(L > 0.f ? acc[0] / L : 0.f, L > 0.f ? acc[PER - 1] / L : 0.f);
