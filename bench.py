@@ -358,6 +358,7 @@ def main():
             ("decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096", dict(kv="e5m2")),
             ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4)),
             ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64)),
+            ("decode_ex_bf16_paged16_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=16)),
             ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),
         ]
         for name, extra in variants:

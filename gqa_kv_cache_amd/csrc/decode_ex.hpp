@@ -10,11 +10,12 @@
 //     [max(0, pos - W + 1), pos] (W = window, 0 = all): causal among the new
 //     tokens as in prefill ("从MHA到GQA", causal mask section), restricted to
 //     a window when one is given.
-//   - Every 32-key step of a wave gets its own buffer resource based at the
-//     step's first row: in a paged cache that row lives in block
-//     block_table[b][key0 / block_size] (block_size a multiple of 32, so a
-//     step never crosses a block).  The resource's size ends at the last
-//     valid row, so rows at or past the split end read as zero.
+//   - Each 16-row half of a wave's 32-key step gets its own buffer resource
+//     based at the half's first row: in a paged cache that row lives in
+//     block block_table[b][row / block_size] (block_size a multiple of 16,
+//     so a half never crosses a block; the two halves may lie in different
+//     blocks).  A resource's size ends at the last valid row, so rows at or
+//     past the split end read as zero.
 //   - FP8 rows are converted to bf16 (exact: every E4M3 and every E5M2 value
 //     is a bf16 value) when K is staged in LDS and when the V fragments are built.  The
 //     per-KV-head scales never touch the elements: k_scale multiplies the
@@ -78,21 +79,36 @@ template <int D, bool KV8> struct ExStepData {
     typename ExVRaw<D, KV8>::T vB[2][4];
 };
 
-// Loads of one 32-key step; offsets are relative to the step's first row.
-template <int D, bool KV8>
-__device__ __forceinline__ void ex_load_step(ExStepData<D, KV8>& st, __amdgpu_buffer_rsrc_t kr,
-                                             __amdgpu_buffer_rsrc_t vr, int rs, int lane) {
+// Loads of one 32-key step.  kr[x], vr[x] cover rows 16x .. 16x+15 of the
+// step.  H16: two resources, each based at its half's first row (the halves
+// may lie in different cache blocks); otherwise one resource for the whole
+// step (both entries equal).  A whole-row K load covers RPI rows (4, 8 or
+// 16, a divisor of 16), so it stays in one half.
+template <int D, bool KV8, bool H16>
+__device__ __forceinline__ void ex_load_step(ExStepData<D, KV8>& st, const __amdgpu_buffer_rsrc_t (&kr)[2],
+                                             const __amdgpu_buffer_rsrc_t (&vr)[2], int rs, int lane) {
     typedef ExShape<D, KV8> Sh;
+    static_assert(16 % Sh::RPI == 0, "a K load must not straddle the two halves of a step");
     const int col = lane & 15, grp = lane >> 4;
     const int vk = (lane / Sh::CPR) * rs + 16 * (lane % Sh::CPR);
 #pragma unroll
-    for (int i = 0; i < Sh::KLD; ++i)
-        st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, vk, Sh::RPI * i * rs, kStreamLoad);
-    const int vv = 4 * grp * rs + Sh::VB * col;
+    for (int i = 0; i < Sh::KLD; ++i) {
+        const int row = Sh::RPI * i;  // first row of this load within the step
+        if constexpr (H16)
+            st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr[row / 16], vk, (row % 16) * rs, kStreamLoad);
+        else
+            st.kR[i] = __builtin_amdgcn_raw_buffer_load_b128(kr[0], vk, row * rs, kStreamLoad);
+    }
+    const int vv = 4 * grp * rs + Sh::VB * col;  // rows r + 4 grp of a half, r < 4
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st.vB[t][r] = ex_load_v<D, KV8>(vr, vv, (16 * t + r) * rs);
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (H16)
+                st.vB[t][r] = ex_load_v<D, KV8>(vr[t], vv, r * rs);
+            else
+                st.vB[t][r] = ex_load_v<D, KV8>(vr[0], vv, (16 * t + r) * rs);
+        }
 }
 
 // K rows into the wave's LDS tile as bf16, in the plain kernel's swizzled
@@ -226,7 +242,7 @@ __device__ __forceinline__ int ex_first_key(int n, int T, int window) {
 // NT = ceil(T * gsize / 16) tiles of 16 query rows; NWV waves per workgroup
 // take the split's 32-key steps in turn.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int KV, int NWV>
+template <int D, int NT, int KV, int NWV, bool H16>
 __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, const float* __restrict__ k_scale,
@@ -298,21 +314,44 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     const int kbeg = max(start, first & ~31);
     const uint8_t* kseq = kc + (((int64_t)b * Lmax) * Hkv + g) * Ex::ROWB;
     const uint8_t* vseq = vc + (((int64_t)b * Lmax) * Hkv + g) * Ex::ROWB;
-    // Issue the loads of the step starting at key0 (resources sized to its valid rows).
+    // Issue the loads of the step starting at key0, through resources sized
+    // to the valid rows (a resource of size 0 reads zeros only).  A step lies
+    // in one block when the blocks hold a multiple of 32 rows; with 16-row
+    // multiples (H16) each 16-row half gets its own resource, in its block.
     auto load = [&](int key0, ExStepData<D, KV8>& st) __attribute__((always_inline)) {
-        const uint8_t *kp, *vp;
-        if (block_table) {
-            const int64_t blk = block_table[(int64_t)b * max_blocks + key0 / bs];
-            const int64_t off = ((blk * bs + key0 % bs) * Hkv + g) * Ex::ROWB;
-            kp = kc + off;
-            vp = vc + off;
+        __amdgpu_buffer_rsrc_t kr[2], vr[2];
+        if constexpr (H16) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int row0 = key0 + 16 * x;
+                const int valid = min(end - row0, 16);
+                int nbytes = 0;
+                int64_t off = 0;
+                if (valid > 0) {
+                    nbytes = (valid - 1) * rs + Ex::ROWB;
+                    const int64_t blk = block_table[(int64_t)b * max_blocks + row0 / bs];
+                    off = ((blk * bs + row0 % bs) * Hkv + g) * Ex::ROWB;
+                }
+                kr[x] = make_rsrc(kc + off, nbytes);
+                vr[x] = make_rsrc(vc + off, nbytes);
+            }
         } else {
-            kp = kseq + (int64_t)key0 * rs;
-            vp = vseq + (int64_t)key0 * rs;
+            const uint8_t *kp, *vp;
+            if (block_table) {
+                const int64_t blk = block_table[(int64_t)b * max_blocks + key0 / bs];
+                const int64_t off = ((blk * bs + key0 % bs) * Hkv + g) * Ex::ROWB;
+                kp = kc + off;
+                vp = vc + off;
+            } else {
+                kp = kseq + (int64_t)key0 * rs;
+                vp = vseq + (int64_t)key0 * rs;
+            }
+            const int valid = min(end - key0, kDecodeStep);
+            const int nbytes = (valid - 1) * rs + Ex::ROWB;
+            kr[0] = kr[1] = make_rsrc(kp, nbytes);
+            vr[0] = vr[1] = make_rsrc(vp, nbytes);
         }
-        const int valid = min(end - key0, kDecodeStep);
-        const int nbytes = (valid - 1) * rs + Ex::ROWB;
-        ex_load_step<D, KV8>(st, make_rsrc(kp, nbytes), make_rsrc(vp, nbytes), rs, lane);
+        ex_load_step<D, KV8, H16>(st, kr, vr, rs, lane);
     };
     constexpr int stride = NWV * kDecodeStep;
     if constexpr (KV8) {

@@ -128,7 +128,7 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
     if (a->kv_dtype != GQA_BF16 && a->kv_dtype != GQA_FP8_E4M3 && a->kv_dtype != GQA_FP8_E5M2) return GQA_ERR_DTYPE;
     if ((int64_t)a->T * (a->Hq / a->Hkv) > kMaxGroup) return GQA_ERR_UNSUPPORTED;
     if (a->block_table) {
-        if (a->block_size < 32 || a->block_size % 32 != 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
+        if (a->block_size < 16 || a->block_size % 16 != 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
             return GQA_ERR_SHAPE;
         if ((int64_t)a->max_blocks * a->block_size != a->Lmax) return GQA_ERR_SHAPE;
     }
@@ -166,7 +166,7 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
 // (up to 32 query rows; more rows need more registers than 8 waves allow).
 template <bool KV8, int NT> constexpr int ex_waves() { return KV8 && NT <= 2 ? 8 : 4; }
 
-template <int D, int KV>
+template <int D, int KV, bool H16>
 void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_args* a, const ExPlan& p,
                       float c, float* wa, float* wm) {
     dim3 block;
@@ -177,13 +177,34 @@ void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_arg
     const int gs = a->Hq / a->Hkv;
 #define GQA_EX_ARGS q, k, v, a->seqlens, a->k_scale, a->v_scale, a->block_table, a->max_blocks, \
                     a->block_size, a->T, a->Hq, a->Hkv, a->Lmax, gs, p.splits, p.chunk, a->window, c, o, wa, wm
+#define GQA_EX_CASE(N) block = dim3(64 * ex_waves<KV != 0, N>()); \
+    hipLaunchKernelGGL((gqa::decode_ex_kernel<D, N, KV, ex_waves<KV != 0, N>(), H16>), grid, block, 0, hs, GQA_EX_ARGS)
     switch (nt) {
-        case 1: block = dim3(64 * ex_waves<KV != 0, 1>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 1, KV, ex_waves<KV != 0, 1>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        case 2: block = dim3(64 * ex_waves<KV != 0, 2>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 2, KV, ex_waves<KV != 0, 2>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        case 3: block = dim3(64 * ex_waves<KV != 0, 3>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 3, KV, ex_waves<KV != 0, 3>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
-        default: block = dim3(64 * ex_waves<KV != 0, 4>()); hipLaunchKernelGGL((gqa::decode_ex_kernel<D, 4, KV, ex_waves<KV != 0, 4>()>), grid, block, 0, hs, GQA_EX_ARGS); break;
+        case 1: GQA_EX_CASE(1); break;
+        case 2: GQA_EX_CASE(2); break;
+        case 3: GQA_EX_CASE(3); break;
+        default: GQA_EX_CASE(4); break;
     }
+#undef GQA_EX_CASE
 #undef GQA_EX_ARGS
+}
+
+// Cache format and block shape -> kernel.  H16: paged blocks of a 16-row
+// multiple that is not a 32-row one, so a 32-key step may span two blocks.
+template <int D>
+void launch_decode_ex_for(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_args* a, const ExPlan& p,
+                          float c, float* wa, float* wm) {
+    const bool h16 = a->block_table != nullptr && a->block_size % 32 != 0;
+    if (a->kv_dtype == GQA_FP8_E4M3) {
+        if (h16) launch_decode_ex<D, 1, true>(nt, grid, hs, a, p, c, wa, wm);
+        else launch_decode_ex<D, 1, false>(nt, grid, hs, a, p, c, wa, wm);
+    } else if (a->kv_dtype == GQA_FP8_E5M2) {
+        if (h16) launch_decode_ex<D, 2, true>(nt, grid, hs, a, p, c, wa, wm);
+        else launch_decode_ex<D, 2, false>(nt, grid, hs, a, p, c, wa, wm);
+    } else {
+        if (h16) launch_decode_ex<D, 0, true>(nt, grid, hs, a, p, c, wa, wm);
+        else launch_decode_ex<D, 0, false>(nt, grid, hs, a, p, c, wa, wm);
+    }
 }
 
 template <int ROWB>
@@ -350,15 +371,8 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
     const int nt = (a->T * (a->Hq / a->Hkv) + 15) / 16;
     const float c = a->scale * gqa::kLog2e;
     dim3 grid((unsigned)((int64_t)a->B * a->Hkv * S));
-    if (a->d == 128) {
-        if (a->kv_dtype == GQA_FP8_E4M3) launch_decode_ex<128, 1>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else if (a->kv_dtype == GQA_FP8_E5M2) launch_decode_ex<128, 2>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else launch_decode_ex<128, 0>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-    } else {
-        if (a->kv_dtype == GQA_FP8_E4M3) launch_decode_ex<64, 1>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else if (a->kv_dtype == GQA_FP8_E5M2) launch_decode_ex<64, 2>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-        else launch_decode_ex<64, 0>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
-    }
+    if (a->d == 128) launch_decode_ex_for<128>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
+    else launch_decode_ex_for<64>(nt, grid, hs, a, plan, c, ws_acc, ws_ml);
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     if (S > 1) {
         dim3 mgrid((unsigned)rows);

@@ -169,7 +169,7 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P
  *   seqlens  [B] int32: valid rows per sequence AFTER the append.
  *            Precondition (not checked, device data): T <= seqlens[b] <= Lmax.
  *   block_table  [B, max_blocks] int32 or NULL.  block_size must be a multiple
- *            of 32; Lmax must equal max_blocks * block_size.  Precondition:
+ *            of 16; Lmax must equal max_blocks * block_size.  Precondition:
  *            every entry used is in [0, num_blocks).
  *   k_scale, v_scale  [Hkv] fp32, the FP8 formats only (required there,
  *            ignored for bf16): K row values are fp8(byte) * k_scale[g], V

@@ -195,7 +195,8 @@ def _ex_args(**kw):
     (dict(dtype=gqa.F32), Status.ERR_DTYPE),
     (dict(kv_dtype=gqa.F32), Status.ERR_DTYPE),
     (dict(T=17, Hq=8, Hkv=2), Status.ERR_UNSUPPORTED),           # 17 tokens x group of 4 > 64 rows
-    (dict(block_table=FAKE, block_size=16, max_blocks=4, num_blocks=8), Status.ERR_SHAPE),
+    (dict(block_table=FAKE, block_size=8, max_blocks=8, num_blocks=8), Status.ERR_SHAPE),    # not a multiple of 16
+    (dict(block_table=FAKE, block_size=24, max_blocks=3, num_blocks=8, Lmax=72), Status.ERR_SHAPE),
     (dict(block_table=FAKE, block_size=32, max_blocks=3, num_blocks=8), Status.ERR_SHAPE),  # Lmax != 96
     (dict(block_table=FAKE, block_size=32, max_blocks=2, num_blocks=0), Status.ERR_SHAPE),
     (dict(num_splits=65), Status.ERR_UNSUPPORTED),

@@ -140,10 +140,11 @@ def test_fp8_dtypes_name_their_format():
 
 
 @pytest.mark.parametrize("kv", ["same", "fp8", "e5m2"])
-@pytest.mark.parametrize("block_size", [32, 64, 128])
+@pytest.mark.parametrize("block_size", [16, 32, 48, 64, 128])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_paged(kv, block_size, splits):
-    c = case(kv=kv, paged=True, block_size=block_size, T=2, seed=44)
+    Lmax = -(-256 // block_size) * block_size   # whole blocks (288 for 48-row blocks)
+    c = case(kv=kv, paged=True, block_size=block_size, T=2, Lmax=Lmax, seed=44)
     out, _, _ = run_ex(c, num_splits=splits)
     check(c, from_dev(out), oracle_ex(c))
 
@@ -156,19 +157,21 @@ def test_window(window, splits):
     check(c, from_dev(out), oracle_ex(c))
 
 
-@pytest.mark.parametrize("kv", ["fp8", "e5m2"])
-def test_everything_together(kv):
-    c = case(B=4, T=4, Hq=32, Hkv=4, kv=kv, paged=True, block_size=32, window=45,
+@pytest.mark.parametrize("kv,block_size", [("fp8", 32), ("e5m2", 32), ("same", 16), ("fp8", 16)])
+def test_everything_together(kv, block_size):
+    c = case(B=4, T=4, Hq=32, Hkv=4, kv=kv, paged=True, block_size=block_size, window=45,
              seqlens=(256, 161, 64, 4), seed=46)
     for splits in (0, 1, 5):
         out, _, _ = run_ex(c, num_splits=splits)
         check(c, from_dev(out), oracle_ex(c))
 
 
-@pytest.mark.parametrize("kv,paged", [("same", False), ("same", True), ("fp8", False), ("fp8", True),
-                                      ("e5m2", False), ("e5m2", True)])
-def test_append_writes_cache_rows_exactly(kv, paged):
-    c = case(kv=kv, paged=paged, T=4, seed=47)
+@pytest.mark.parametrize("kv,paged,block_size", [("same", False, 64), ("same", True, 64),
+                                                 ("fp8", False, 64), ("fp8", True, 64),
+                                                 ("e5m2", False, 64), ("e5m2", True, 64),
+                                                 ("same", True, 16), ("fp8", True, 16)])
+def test_append_writes_cache_rows_exactly(kv, paged, block_size):
+    c = case(kv=kv, paged=paged, block_size=block_size, T=4, seed=47)
     out, k, v = run_ex(c, append=True)
     want_k, want_v = c.k_pre.copy(), c.v_pre.copy()
     orc.append(want_k, want_v, c.k_new, c.v_new, c.seqlens, block_table=c.block_table,
@@ -214,3 +217,28 @@ def test_run_twice_bitwise():
     a, _, _ = run_ex(c, num_splits=3)
     b, _, _ = run_ex(c, num_splits=3)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["same", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged16_halves_in_different_blocks(kv, d):
+    """16-row blocks: the two halves of every 32-key step come from blocks
+    the random permutation put far apart; lengths end inside either half."""
+    c = case(B=4, T=2, Hq=16, Hkv=2, d=d, Lmax=192, seqlens=(192, 177, 161, 2), kv=kv,
+             paged=True, block_size=16, seed=54)
+    for splits in (0, 1, 3):
+        out, _, _ = run_ex(c, num_splits=splits)
+        check(c, from_dev(out), oracle_ex(c))
+
+
+def test_paged16_70b_layer_sampled():
+    """The 70B-class layer shape in a pool of 16-row blocks, 4 new tokens,
+    sampled rows against the oracle."""
+    c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096 - 7 * i for i in range(32)], "bf16",
+                          seed=55, paged=True, block_size=16, invalid="zero",
+                          name="ex_paged16_B32_T4_Hq64_Hkv8_d128_L4096")
+    out, _, _ = run_ex(c)
+    rng = np.random.default_rng(8)
+    rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))
+    got = from_dev(out).reshape(-1, 128)[rows]
+    check(c, got, oracle_ex(c, rows=rows))
