@@ -242,3 +242,30 @@ def test_paged16_70b_layer_sampled():
     rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))
     got = from_dev(out).reshape(-1, 128)[rows]
     check(c, got, oracle_ex(c, rows=rows))
+
+
+# The extended workloads the benchmark times (70B-class layer shape, seed 60,
+# zero beyond each length), in the same launch configuration (automatic
+# splits), on sampled rows.
+L70 = dict(B=32, T=1, Hq=64, Hkv=8, d=128, Lmax=4096, seqlens=[4096] * 32, dtype="bf16",
+           invalid="zero")
+
+
+@pytest.mark.parametrize("name,extra", [
+    ("decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096", dict(kv="fp8")),
+    ("decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096", dict(kv="e5m2")),
+    ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4)),
+    ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64)),
+    ("decode_ex_bf16_paged16_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=16)),
+    ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),
+])
+def test_benchmark_extended_workloads_sampled(name, extra):
+    a = dict(L70)
+    a.update(extra)
+    c = gi.decode_ex_case(seed=60, name=name, **a)
+    out, _, _ = run_ex(c, append=False)
+    T = c.q.shape[1]
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(32 * T * 64, 64, replace=False))
+    got = from_dev(out).reshape(-1, 128)[rows]
+    check(c, got, oracle_ex(c, rows=rows))
