@@ -133,6 +133,9 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
         if ((int64_t)a->max_blocks * a->block_size != a->Lmax) return GQA_ERR_SHAPE;
     }
     if (a->num_splits < 0 || a->num_splits > a->Lmax) return GQA_ERR_UNSUPPORTED;
+    // the rows of one 32-key step are addressed with 32-bit byte offsets
+    const int64_t elt = a->kv_dtype == GQA_BF16 ? 2 : 1;
+    if ((int64_t)gqa::kDecodeStep * a->Hkv * a->d * elt > INT_MAX) return GQA_ERR_SHAPE;
     int64_t chunk;
     if (a->num_splits == 0) {
         int cus = 0;
@@ -156,7 +159,7 @@ gqa_status plan_decode_ex(const gqa_decode_ex_args* a, bool query_device, ExPlan
     if ((int64_t)a->B * a->Hkv * splits > INT_MAX || rows > INT_MAX) return GQA_ERR_SHAPE;
     plan->splits = (int)splits;
     plan->chunk = (int)chunk;
-    plan->elt = a->kv_dtype == GQA_BF16 ? 2 : 1;
+    plan->elt = (int)elt;
     plan->ws_bytes = splits > 1 ? (size_t)rows * splits * (a->d + 2) * sizeof(float) : 0;
     return GQA_OK;
 }

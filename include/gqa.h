@@ -177,7 +177,10 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P
  *   k_new, v_new  [B, T, Hkv, d] in kv_dtype, or both NULL.  When given they
  *            are first stored, byte for byte, at rows seqlens[b] - T + t.
  *   window   0 = every key; W > 0 = the last W keys of each token.
- *   T * (Hq/Hkv) <= 64; d 64 or 128; B, T, Hq, Hkv, Lmax >= 1.
+ *   T * (Hq/Hkv) <= 64; d 64 or 128; B, T, Hq, Hkv, Lmax >= 1;
+ *            32 * Hkv * d * (bytes per cache element) <= 2^31 - 1 (the rows of
+ *            one 32-key step are addressed with 32-bit offsets), else
+ *            GQA_ERR_SHAPE.
  *   num_splits, workspace, workspace_bytes  as for gqa_decode; the size comes
  *            from gqa_decode_ex_workspace_size.
  *

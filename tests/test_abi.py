@@ -190,6 +190,7 @@ def _ex_args(**kw):
     (dict(T=0), Status.ERR_SHAPE),
     (dict(window=-1), Status.ERR_SHAPE),
     (dict(B=0), Status.ERR_SHAPE),
+    (dict(Hq=524288, Hkv=524288), Status.ERR_SHAPE),                # 32 rows x 128 MiB > 2^31 - 1
     (dict(Hq=6, Hkv=4), Status.ERR_GROUP),
     (dict(d=32), Status.ERR_HEADDIM),
     (dict(dtype=gqa.F32), Status.ERR_DTYPE),
