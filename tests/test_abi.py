@@ -255,3 +255,25 @@ def test_prefill_ex_validation(kw, expect):
                                    a["d"], a["causal"], a["window"], a["scale"], a["dt"], a["out"],
                                    a["stream"])
     assert st == expect
+
+
+# --- binding: cache element codes (host logic, no device needed) ------------
+
+def test_kv_code_mapping():
+    import torch
+    from gqa_kv_cache_amd._native import _kv_code
+    u8 = torch.zeros(4, dtype=torch.uint8)
+    assert _kv_code(u8, None) == gqa.FP8_E4M3
+    assert _kv_code(u8, "e4m3") == gqa.FP8_E4M3
+    assert _kv_code(u8, "e5m2") == gqa.FP8_E5M2
+    assert _kv_code(u8.view(torch.float8_e5m2), None) == gqa.FP8_E5M2
+    assert _kv_code(u8.view(torch.float8_e4m3fn), "e4m3") == gqa.FP8_E4M3
+    assert _kv_code(torch.zeros(4, dtype=torch.bfloat16), None) == gqa.BF16
+    with pytest.raises(TypeError):
+        _kv_code(u8.view(torch.float8_e4m3fn), "e5m2")
+    with pytest.raises(TypeError):
+        _kv_code(torch.zeros(4, dtype=torch.bfloat16), "e4m3")
+    with pytest.raises(ValueError):
+        _kv_code(u8, "e3m4")
+    with pytest.raises(TypeError):
+        _kv_code(torch.zeros(4, dtype=torch.float16), None)
