@@ -108,8 +108,17 @@ void launch_split_bf16(int nt, dim3 grid, hipStream_t st, const uint16_t* q, con
         case 1: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 1>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
         case 2: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 2>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
         case 3: hipLaunchKernelGGL((gqa::decode_split_bf16<D, 3>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
-        // four tiles: one per wave, no combine across waves
-        default: hipLaunchKernelGGL((gqa::decode_split_bf16_tiles<D>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm); break;
+        // Four tiles.  Short pieces: one tile per wave, so no partial sums
+        // are combined across waves (the combine would dominate).  Pieces of
+        // 512 keys or more: the waves split the keys as for fewer tiles,
+        // which reads each row once instead of once per tile (about 10%
+        // faster for 64-head groups at 512-1024-key pieces).
+        default:
+            if (chunk >= 512)
+                hipLaunchKernelGGL((gqa::decode_split_bf16<D, 4>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm);
+            else
+                hipLaunchKernelGGL((gqa::decode_split_bf16_tiles<D>), grid, block, 0, st, q, k, v, sl, Hq, Hkv, Lmax, gs, S, chunk, c, out, wa, wm);
+            break;
     }
 }
 

@@ -136,6 +136,20 @@ def test_long_two_sequences(splits):
     check(c, from_dev(run_decode(c, splits)), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,lens,splits", [
+    (32, 64, 1, 4096, None, 0),                  # automatic: 8 pieces of 512 keys
+    (3, 57, 1, 1100, [1100, 700, 513], 2),       # partly empty last head tile, 550-key pieces
+    (2, 128, 2, 1536, [1536, 1000], 1),          # one 1536-key piece
+])
+def test_four_head_tiles_long_pieces(B, Hq, Hkv, L, lens, splits):
+    """Groups of 49-64 heads with pieces of 512 keys or more (the waves split
+    the keys and combine four tiles of partial sums)."""
+    lens = lens or [L] * B
+    c = gi.decode_case(B, Hq, Hkv, 128, L, lens, "bf16", q_seed=13, kv_seed=14, invalid="nan",
+                       name="tiles4_long_B%d_Hq%d_Hkv%d_L%d_s%d" % (B, Hq, Hkv, L, splits))
+    check(c, from_dev(run_decode(c, splits)), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
+
+
 def test_one_key_per_split():
     c = gi.decode_case(3, 8, 2, 128, 100, [100, 57, 1], "bf16", q_seed=7, kv_seed=8, invalid="nan")
     check(c, from_dev(run_decode(c, 100)), orc.decode(c.q, c.k, c.v, c.seqlens, c.scale))
