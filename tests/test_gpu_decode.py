@@ -205,3 +205,57 @@ def test_run_twice_bitwise(splits):
     a = bits(run_decode(c, splits))
     b = bits(run_decode(c, splits))
     assert np.array_equal(a, b)
+
+
+def test_concurrent_threads_and_streams_bitwise():
+    """Two host threads, each on its own stream (default priority), issue
+    decode and extended-decode calls back to back; every output equals the
+    single-stream result bit for bit (the calls keep no shared state)."""
+    import threading
+    c1 = gi.decode_case(4, 32, 8, 128, 1000, [1000, 999, 3, 640], "bf16", q_seed=21, kv_seed=22,
+                        invalid="nan")
+    c2 = gi.decode_ex_case(3, 2, 16, 4, 128, 256, [256, 97, 5], "bf16", seed=23, kv="fp8",
+                           paged=True, block_size=16, window=50)
+    want1 = bits(run_decode(c1, 3))
+
+    def ex_args():
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda() if a.dtype == np.uint8 else to_dev(a)
+        return (to_dev(c2.q), d(c2.k), d(c2.v), torch.from_numpy(c2.seqlens).cuda(),
+                dict(scale=c2.scale, k_scale=torch.from_numpy(c2.k_scale).cuda(),
+                     v_scale=torch.from_numpy(c2.v_scale).cuda(),
+                     block_table=torch.from_numpy(c2.block_table).cuda(), block_size=16, window=50))
+
+    q2, k2, v2, sl2, kw2 = ex_args()
+    want2 = bits(gqa.decode_ex(q2, k2, v2, sl2, num_splits=2, **kw2))
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(name):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                if name == "decode":
+                    q, k, v = to_dev(c1.q), to_dev(c1.k), to_dev(c1.v)
+                    sl = torch.from_numpy(c1.seqlens).cuda()
+                    outs = [gqa.decode(q, k, v, sl, c1.scale, num_splits=3) for _ in range(20)]
+                else:
+                    q, k, v, sl, kw = ex_args()
+                    outs = [gqa.decode_ex(q, k, v, sl, num_splits=2, **kw) for _ in range(20)]
+            s.synchronize()
+            results[name] = [bits(o) for o in outs]
+        except Exception as e:  # surfaced below, in the test's own thread
+            errors.append(repr(e))
+
+    ts = [threading.Thread(target=worker, args=(n,)) for n in ("decode", "ex")]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert all(np.array_equal(o, want1) for o in results["decode"])
+    assert all(np.array_equal(o, want2) for o in results["ex"])
+    ok, err = bf16_tol_ok(widen(want2.view(np.uint16)).reshape(c2.q.shape),
+                          orc.decode_ex(c2.q, c2.k, c2.v, c2.seqlens, c2.scale, k_scale=c2.k_scale,
+                                        v_scale=c2.v_scale, block_table=c2.block_table,
+                                        block_size=16, window=50))
+    assert ok, err
