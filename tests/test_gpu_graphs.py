@@ -75,3 +75,20 @@ def test_decode_ex_append_fp8_paged_in_a_graph():
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), bits(want)), i
         assert torch.equal(k, k2) and torch.equal(v, v2)
+
+
+def test_prefill_with_window_in_a_graph():
+    c = gi.prefill_case(2, 333, 16, 4, 128, "bf16", seed=35)
+    q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
+    out = torch.empty_like(q)
+    g = _capture(lambda: gqa.prefill(q, k, v, True, c.scale, out=out, window=100))
+    q_other = to_dev(gi.prefill_case(2, 333, 16, 4, 128, "bf16", seed=36).q)
+    for i in range(4):
+        src = q_other if i % 2 else to_dev(c.q)
+        q.copy_(src)
+        want = gqa.prefill(src, k, v, True, c.scale, window=100)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(want)), i
