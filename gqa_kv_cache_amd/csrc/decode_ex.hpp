@@ -125,7 +125,7 @@ __device__ __forceinline__ void ex_stage_k(const ExStepData<D, KV != 0>& st, u32
         if constexpr (!KV8) {
             kt[kl * CPR16 + (c ^ (kl % CPR16))] = st.kR[i];
         } else {
-            // 16 E4M3 values = head dims 16c .. 16c+15 = bf16 chunks 2c, 2c+1
+            // 16 FP8 values = head dims 16c .. 16c+15 = bf16 chunks 2c, 2c+1
             const u32x4 w = st.kR[i];
             const u32x4 lo = u32x4{fp8x2_to_bf16x2<KV, false>(w[0]), fp8x2_to_bf16x2<KV, true>(w[0]),
                                    fp8x2_to_bf16x2<KV, false>(w[1]), fp8x2_to_bf16x2<KV, true>(w[1])};
@@ -238,7 +238,7 @@ __device__ __forceinline__ int ex_first_key(int n, int T, int window) {
 
 // ---------------------------------------------------------------------------
 // Split kernel.  q [B,T,Hq,d] bf16; caches contiguous [B,Lmax,Hkv,d] or a
-// paged pool [nblocks,bs,Hkv,d] (bf16 or E4M3 bytes); out [B,T,Hq,d] bf16.
+// paged pool [nblocks,bs,Hkv,d] (bf16 or FP8 bytes); out [B,T,Hq,d] bf16.
 // NT = ceil(T * gsize / 16) tiles of 16 query rows; NWV waves per workgroup
 // take the split's 32-key steps in turn.
 // ---------------------------------------------------------------------------
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     };
     constexpr int stride = NWV * kDecodeStep;
     if constexpr (KV8) {
-        // An E4M3 step moves half the bytes of a bf16 one: keep the next
+        // An FP8 step moves half the bytes of a bf16 one: keep the next
         // step's loads in flight while the current step is computed, so a
         // wave has as many bytes outstanding as in the bf16 kernel.
         ExStepData<D, KV8> cur;
