@@ -30,6 +30,7 @@ class Status(enum.IntEnum):
     ERR_WORKSPACE = 7
     ERR_UNSUPPORTED = 8
     ERR_HIP = 9
+    ERR_SCRATCH_LIMIT = 10
 
 
 class GqaError(RuntimeError):
@@ -45,7 +46,7 @@ EXPORTS = (
     "gqa_status_str", "gqa_decode", "gqa_decode_num_splits", "gqa_decode_workspace_size",
     "gqa_prefill", "gqa_kv_cache_elems", "gqa_decode_bytes", "gqa_decode_flops",
     "gqa_prefill_flops", "gqa_prefill_bytes", "gqa_decode_ex", "gqa_decode_ex_workspace_size",
-    "gqa_prefill_ex",
+    "gqa_prefill_ex", "gqa_decode_noalloc",
 )
 
 
@@ -80,6 +81,8 @@ def load():
     lib.gqa_status_str.restype = ctypes.c_char_p
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
     lib.gqa_decode.restype = ci
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, ci, vp]
+    lib.gqa_decode_noalloc.restype = ci
     lib.gqa_decode_num_splits.argtypes = [ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
     lib.gqa_decode_num_splits.restype = ci
     lib.gqa_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
@@ -145,14 +148,10 @@ def decode_workspace_size(B, Hq, Hkv, d, Lmax, dtype_code, num_splits=0) -> int:
     return out.value
 
 
-def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, workspace=None):
-    """GQA decode step.  q [B,Hq,d]; k_cache, v_cache [B,Lmax,Hkv,d]; seqlens [B] int32.
-
-    All tensors on one device; q, caches and out share one dtype (float32 or
-    bfloat16).  Runs on the device's current stream; returns ``out``.
-    """
+def _decode_shapes(q, k_cache, v_cache, seqlens, out):
+    """Shape and dtype checks shared by decode and decode_noalloc; returns
+    (B, Hq, Hkv, d, Lmax, dtype code)."""
     import torch
-    lib = load()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens)):
         _require_cuda(name, t)
     if seqlens.dtype != torch.int32:
@@ -166,14 +165,26 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, wor
     dt = _dtype_code(q)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("gqa: q and the caches must share one dtype")
+    if out is not None:
+        _require_cuda("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("gqa: out must match q in shape and dtype")
+    return B, Hq, Hkv, d, Lmax, dt
+
+
+def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, workspace=None):
+    """GQA decode step.  q [B,Hq,d]; k_cache, v_cache [B,Lmax,Hkv,d]; seqlens [B] int32.
+
+    All tensors on one device; q, caches and out share one dtype (float32 or
+    bfloat16).  Runs on the device's current stream; returns ``out``.
+    """
+    import torch
+    lib = load()
+    B, Hq, Hkv, d, Lmax, dt = _decode_shapes(q, k_cache, v_cache, seqlens, out)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    else:
-        _require_cuda("out", out)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("gqa: out must match q in shape and dtype")
     with torch.cuda.device(q.device):
         need = decode_workspace_size(B, Hq, Hkv, d, Lmax, dt, num_splits)
         ws_ptr, ws_bytes = None, 0
@@ -187,6 +198,27 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, wor
                             B, Hq, Hkv, d, Lmax, float(scale), dt, out.data_ptr(), ws_ptr, ws_bytes,
                             int(num_splits), stream)
     _check(st, "gqa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens, out, scale=None, num_splits=0):
+    """GQA decode step through gqa_decode_noalloc: like ``decode``, but the
+    split partials live in the library's static device scratch, so neither
+    the call nor this wrapper allocates.  ``out`` is required.  Calls that
+    overlap on one GPU share that scratch and race."""
+    import torch
+    lib = load()
+    B, Hq, Hkv, d, Lmax, dt = _decode_shapes(q, k_cache, v_cache, seqlens, out)
+    if out is None:
+        raise ValueError("gqa: decode_noalloc writes into a caller-provided out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    seqlens.data_ptr(), B, Hq, Hkv, d, Lmax, float(scale), dt,
+                                    out.data_ptr(), int(num_splits), stream)
+    _check(st, "gqa_decode_noalloc")
     return out
 
 

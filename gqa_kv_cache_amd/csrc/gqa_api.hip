@@ -228,6 +228,43 @@ void launch_append(hipStream_t hs, const gqa_decode_ex_args* a) {
                        a->seqlens, a->block_table, a->max_blocks, a->block_size, a->T, a->Hkv, a->Lmax);
 }
 
+gqa_status validate_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax,
+                           gqa_dtype dtype, const void* out, int num_splits, DecodePlan* plan);
+gqa_status run_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax, float scale,
+                      gqa_dtype dtype, void* out, void* workspace, const DecodePlan& plan,
+                      void* stream);
+
+// ----- static scratch of gqa_decode_noalloc (the array itself is below) -----
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+}  // namespace
+
+// The split partials of gqa_decode_noalloc live in this array instead of a
+// caller buffer.  Every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a host
+// stand-in, never the device memory: kernels and copies get the address
+// hipGetSymbolAddress returns for the current device, cached per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+gqa_status scratch_address(void** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // Resolving the symbol twice from racing threads is harmless: both
+        // get the same address.
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GQA_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,6 +281,7 @@ const char* gqa_status_str(gqa_status s) {
         case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
         case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: group size above 64 or num_splits out of range";
         case GQA_ERR_HIP: return "GQA_ERR_HIP: the HIP runtime reported an error";
+        case GQA_ERR_SCRATCH_LIMIT: return "GQA_ERR_SCRATCH_LIMIT: the split partials exceed the static scratch of gqa_decode_noalloc";
     }
     return "GQA status: unknown code";
 }
@@ -272,6 +310,44 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax, float scale,
                       gqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
                       int num_splits, void* stream) {
+    DecodePlan plan;
+    gqa_status st = validate_decode(q, k_cache, v_cache, seqlens, B, Hq, Hkv, d, Lmax, dtype, out,
+                                    num_splits, &plan);
+    if (st != GQA_OK) return st;
+    const size_t need = workspace_bytes_for(B, Hq, d, plan.splits);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return GQA_ERR_WORKSPACE;
+    return run_decode(q, k_cache, v_cache, seqlens, B, Hq, Hkv, d, Lmax, scale, dtype, out,
+                      need ? workspace : nullptr, plan, stream);
+}
+
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax,
+                              float scale, gqa_dtype dtype, void* out, int num_splits,
+                              void* stream) {
+    DecodePlan plan;
+    gqa_status st = validate_decode(q, k_cache, v_cache, seqlens, B, Hq, Hkv, d, Lmax, dtype, out,
+                                    num_splits, &plan);
+    if (st != GQA_OK) return st;
+    const size_t need = workspace_bytes_for(B, Hq, d, plan.splits);
+    if (need > kScratchBytes) return GQA_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(&ws);
+        if (st != GQA_OK) return st;
+    }
+    return run_decode(q, k_cache, v_cache, seqlens, B, Hq, Hkv, d, Lmax, scale, dtype, out, ws,
+                      plan, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two decode entry points, then the plan.
+gqa_status validate_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax,
+                           gqa_dtype dtype, const void* out, int num_splits, DecodePlan* plan) {
     if (!q || !k_cache || !v_cache || !seqlens || !out) return GQA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return GQA_ERR_ALIGN;
@@ -281,21 +357,24 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
     if (st != GQA_OK) return st;
     if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_DTYPE;
     if (num_splits < 0 || num_splits > Lmax) return GQA_ERR_UNSUPPORTED;
-    DecodePlan plan;  // queries the device only when num_splits == 0
-    st = plan_decode(B, Hq, Hkv, d, Lmax, dtype, num_splits, &plan);
-    if (st != GQA_OK) return st;
-    const size_t need = workspace_bytes_for(B, Hq, d, plan.splits);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-        return GQA_ERR_WORKSPACE;
+    // queries the device only when num_splits == 0
+    return plan_decode(B, Hq, Hkv, d, Lmax, dtype, num_splits, plan);
+}
 
+// Launches of one decode call on a validated plan; `workspace` holds the
+// split partials (NULL when the plan has one piece).
+gqa_status run_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, int B, int Hq, int Hkv, int d, int Lmax, float scale,
+                      gqa_dtype dtype, void* out, void* workspace, const DecodePlan& plan,
+                      void* stream) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int gs = Hq / Hkv;
     const int S = plan.splits;
     const float c = scale * gqa::kLog2e;
-    float* ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-    float* ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                   workspace_acc_bytes(B, Hq, d, S))
-                        : nullptr;
+    float* ws_acc = S > 1 ? static_cast<float*>(workspace) : nullptr;
+    float* ws_ml = S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    workspace_acc_bytes(B, Hq, d, S))
+                         : nullptr;
     dim3 grid((unsigned)((int64_t)B * Hkv * S));
 
     (void)hipGetLastError();  // clear a stale error so the check below is ours
@@ -339,6 +418,10 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
     }
     return GQA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 gqa_status gqa_decode_ex_workspace_size(const gqa_decode_ex_args* a, size_t* bytes) {
     if (!a || !bytes) return GQA_ERR_NULL;

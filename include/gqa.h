@@ -18,7 +18,8 @@
  *   - Every data pointer must be 16-byte aligned (GQA_ERR_ALIGN otherwise).
  *   - The caller owns every buffer.  The library allocates no device memory,
  *     keeps no pointer after return and has no state beyond a per-device
- *     cache of the compute-unit count.
+ *     cache of the compute-unit count and, for gqa_decode_noalloc only, one
+ *     static device array per GPU (see there).
  *   - Calls validate their arguments on the host first; a validation error
  *     returns before any device work, and nothing is written.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
@@ -56,7 +57,8 @@ typedef enum {
     GQA_ERR_ALIGN = 6,       /* a data pointer is not 16-byte aligned */
     GQA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
     GQA_ERR_UNSUPPORTED = 8, /* group size Hq/Hkv above 64, or num_splits out of range */
-    GQA_ERR_HIP = 9          /* the HIP runtime reported an error */
+    GQA_ERR_HIP = 9,         /* the HIP runtime reported an error */
+    GQA_ERR_SCRATCH_LIMIT = 10 /* gqa_decode_noalloc: the split partials exceed its static scratch */
 } gqa_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -100,6 +102,33 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *seqlens, int B, int Hq, int Hkv, int d, int Lmax,
                       float scale, gqa_dtype dtype, void *out, void *workspace,
                       size_t workspace_bytes, int num_splits, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.
+ *
+ * Same arguments, layouts, results and errors as gqa_decode, without the
+ * workspace: when the plan cuts the cached length into several pieces, their
+ * partial results go to a static device array of GQA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * Plans that need more than that (B * Hq * pieces * (d + 2) * 4 bytes, see
+ * gqa_decode_workspace_size) return GQA_ERR_SCRATCH_LIMIT before any device
+ * work; pass num_splits to bound the pieces.  The call issues no allocation
+ * and no memset.  The array's address is resolved once per device, on the
+ * first call made with that device current.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two host threads, a graph replay beside an eager
+ * call) race on it and may return wrong results.  Serialise them, or use
+ * gqa_decode with a workspace per stream.  Nothing in the array needs to be
+ * cleared between calls: a call reads only partials it wrote itself.
+ * ------------------------------------------------------------------------ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *seqlens, int B, int Hq, int Hkv, int d, int Lmax,
+                              float scale, gqa_dtype dtype, void *out, int num_splits,
+                              void *stream);
 
 /* Number of pieces gqa_decode will cut the cached length into for these
  * arguments (num_splits = 0 asks for the automatic choice, which depends on

@@ -84,6 +84,46 @@ def test_decode_validation(kw, expect):
     assert _decode(**kw) == expect
 
 
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, B=2, Hq=8, Hkv=2, d=128, Lmax=64, scale=0.1,
+             dt=gqa.BF16, out=FAKE, ns=1, stream=None)
+    a.update(kw)
+    return gqa.load().gqa_decode_noalloc(a["q"], a["k"], a["v"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                                         a["d"], a["Lmax"], a["scale"], a["dt"], a["out"], a["ns"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), Status.ERR_NULL),
+    (dict(out=None), Status.ERR_NULL),
+    (dict(v=FAKE + 2), Status.ERR_ALIGN),
+    (dict(B=0), Status.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), Status.ERR_GROUP),
+    (dict(d=96), Status.ERR_HEADDIM),
+    (dict(dt=gqa.FP8_E4M3), Status.ERR_DTYPE),
+    (dict(ns=65), Status.ERR_UNSUPPORTED),
+    (dict(Lmax=2097121), Status.ERR_SHAPE),
+    # partials of 2 x 8 heads x 64 pieces x (128 + 2) x 4 B = 532,480 B fit; at
+    # 64 x 64 heads x 64 pieces they take 136 MB, above the 16 MiB scratch
+    (dict(B=64, Hq=64, Hkv=8, ns=64), Status.ERR_SCRATCH_LIMIT),
+    (dict(B=2, Hq=512, Hkv=8, Lmax=8192, ns=64), Status.ERR_SCRATCH_LIMIT),
+])
+def test_decode_noalloc_validation(kw, expect):
+    """Every error returns before the library touches the device."""
+    assert _decode_noalloc(**kw) == expect
+
+
+def test_noalloc_scratch_limit_is_the_documented_size():
+    text = open(HEADER).read()
+    assert re.search(r"#define GQA_NOALLOC_SCRATCH_BYTES \(\(size_t\)16 << 20\)", text)
+    limit = 16 << 20
+    # B * Hq * pieces * (d + 2) * 4 bytes: 2 x 64 x 252 x 130 x 4 = 16,773,120 fits,
+    # 253 pieces (16,839,680) do not
+    assert gqa.decode_workspace_size(2, 64, 8, 128, 252, gqa.BF16, 252) == 16773120 <= limit
+    assert gqa.decode_workspace_size(2, 64, 8, 128, 253, gqa.BF16, 253) == 16839680 > limit
+    assert _decode_noalloc(B=2, Hq=64, Hkv=8, Lmax=253, ns=253) == Status.ERR_SCRATCH_LIMIT
+
+
 def _prefill(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, P=16, Hq=8, Hkv=2, d=128, causal=1, scale=0.1,
              dt=gqa.BF16, out=FAKE, stream=None)
