@@ -64,6 +64,19 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Set the OpenMP thread count of later calls (n >= 1); returns the previous one. */
+int oracle_set_threads(int n)
+{
+    const int prev = oracle_num_threads();
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 /*
  * Attention of one query row over n key/value rows.
  *   qrow   : element offset of the query row in q
@@ -434,11 +447,48 @@ static double orc_kv_elem(const void *base, int64_t idx, int dtype, int kv_fmt, 
     return orc_elem(base, idx, dtype);
 }
 
+/*
+ * Error-model terms of one output row, for the tests' derived tolerances only
+ * (nothing here feeds the output).  With w_j / Z the softmax weights of the
+ * row's n visible keys (w as left by the softmax above) and o its output:
+ *   t[c]       = sum_j (w_j / Z) |v_jc - o_c|   (weighted spread of V about o)
+ *   t[d + c]   = sum_j (w_j / Z) |v_jc|         (weighted mean magnitude of V)
+ *   t[2d]      = scale * max_j sum_c |q_c| |k_jc|  (largest absolute score sum)
+ * Rounding the weights by a relative e moves the output by at most e * t[c]
+ * when numerator and denominator share the rounded weights, by e * t[d + c]
+ * when only the numerator does; t[2d] bounds the size of a score's rounding.
+ */
+static void orc_error_terms(const void *q, int64_t qrow, const void *k, const void *v,
+                            int64_t b, int64_t lo, int64_t n, int64_t g, int64_t Hkv, int64_t d,
+                            int64_t Lmax, const int32_t *block_table, int64_t max_blocks,
+                            int64_t bs, double scale, int dtype, int kv_fmt, double ks, double vs,
+                            const double *w, double z, const double *o, double *t)
+{
+    double kappa = 0.0;
+    for (int64_t c = 0; c < 2 * d; ++c)
+        t[c] = 0.0;
+    for (int64_t jj = 0; jj < n; ++jj) {
+        const int64_t r = orc_row_ex(b, lo + jj, g, Hkv, d, Lmax, block_table, max_blocks, bs);
+        const double wj = w[jj] / z;
+        double sabs = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            const double vc = orc_kv_elem(v, r + c, dtype, kv_fmt, vs);
+            t[c] += wj * fabs(vc - o[c]);
+            t[d + c] += wj * fabs(vc);
+            sabs += fabs(orc_elem(q, qrow + c, dtype)) * fabs(orc_kv_elem(k, r + c, dtype, kv_fmt, ks));
+        }
+        if (sabs > kappa)
+            kappa = sabs;
+    }
+    t[2 * d] = fabs(scale) * kappa;
+}
+
 int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t *seqlens,
                      int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t d, int64_t Lmax,
                      double scale, int dtype, int kv_fmt, const float *k_scale,
                      const float *v_scale, const int32_t *block_table, int64_t max_blocks,
-                     int64_t bs, int64_t window, const int64_t *rows, int64_t nrows, double *out)
+                     int64_t bs, int64_t window, const int64_t *rows, int64_t nrows, double *out,
+                     double *terms)
 {
     int rc = orc_check_common(B, Hq, Hkv, d, dtype);
     if (rc)
@@ -508,6 +558,10 @@ int oracle_decode_ex(const void *q, const void *k, const void *v, const int32_t 
                 }
                 for (int64_t c = 0; c < d; ++c)
                     o[c] = acc[c] / z;
+                if (terms)
+                    orc_error_terms(q, qrow, k, v, b, lo, n, g, Hkv, d, Lmax, block_table,
+                                    max_blocks, bs, scale, dtype, kv_fmt, ks, vs, w, z, o,
+                                    terms + i * (2 * d + 1));
             }
         }
         free(w);

@@ -50,7 +50,7 @@ def _bind(lib):
     lib.oracle_mqa_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, dbl, ci, vp]
     lib.oracle_mqa_decode.restype = ci
     lib.oracle_decode_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ci, ci,
-                                     vp, vp, vp, i64, i64, i64, vp, i64, vp]
+                                     vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
     lib.oracle_decode_ex.restype = ci
     lib.oracle_append.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64, i64]
     lib.oracle_append.restype = ci
@@ -60,6 +60,8 @@ def _bind(lib):
     lib.oracle_e5m2_value.restype = dbl
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
+    lib.oracle_set_threads.argtypes = [ci]
+    lib.oracle_set_threads.restype = ci
     return lib
 
 
@@ -107,6 +109,11 @@ class OracleError(RuntimeError):
 def num_threads() -> int:
     """OpenMP threads the oracle runs on (OMP_NUM_THREADS or all cores)."""
     return _load().oracle_num_threads()
+
+
+def set_threads(n: int) -> int:
+    """Run later oracle calls on n OpenMP threads; returns the previous count."""
+    return _load().oracle_set_threads(int(n))
 
 
 def decode(q, k, v, seqlens, scale, rows=None) -> np.ndarray:
@@ -225,7 +232,7 @@ _KV_FORMATS = {"e4m3": 1, "e5m2": 2}
 
 
 def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_table=None,
-              block_size=0, window=0, rows=None, kv_format="e4m3") -> np.ndarray:
+              block_size=0, window=0, rows=None, kv_format="e4m3", terms=False):
     """Extended GQA decode.  q [B,T,Hq,d] (fp32 or bf16 bits).
 
     k, v: contiguous [B,Lmax,Hkv,d] or, with ``block_table`` [B,max_blocks],
@@ -235,6 +242,13 @@ def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_tabl
     seqlens [B] counts the T new tokens; token t sits at seqlens[b]-T+t.
     window > 0 keeps the last ``window`` keys of every token.  Returns
     [B,T,Hq,d] float64, or [len(rows),d] for flat ((b*T+t)*Hq+h) rows.
+
+    terms=True also returns the error-model terms of every output row, for
+    the tests' derived tolerances: (out, sigma, mu, kappa) with sigma, mu
+    shaped like out and kappa one value per row (out's shape without d):
+    sigma_c = sum_j w_j |v_jc - out_c|, mu_c = sum_j w_j |v_jc| (w the
+    normalised softmax weights of the row's visible keys), kappa =
+    |scale| * max_j sum_c |q_c| |k_jc|.  ``out`` is the same either way.
     """
     q, k, v = _c(q), _c(k), _c(v)
     dt = _dtype_code(q)
@@ -266,13 +280,18 @@ def decode_ex(q, k, v, seqlens, scale, *, k_scale=None, v_scale=None, block_tabl
         r = np.ascontiguousarray(rows, dtype=np.int64)
         out = np.empty((r.size, d), np.float64)
         nrows = r.size
+    tm = np.empty((nrows, 2 * d + 1), np.float64) if terms else None
     rc = _load().oracle_decode_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, sl.ctypes.data,
                                   B, T, Hq, Hkv, d, Lmax, float(scale), dt, fmt,
                                   _ptr(ks), _ptr(vs), _ptr(bt), maxb, bs, int(window), _ptr(r),
-                                  nrows, out.ctypes.data)
+                                  nrows, out.ctypes.data, _ptr(tm))
     if rc:
         raise OracleError("oracle_decode_ex returned %d" % rc)
-    return out
+    if not terms:
+        return out
+    shape = out.shape
+    return (out, tm[:, :d].reshape(shape), tm[:, d:2 * d].reshape(shape),
+            tm[:, 2 * d].reshape(shape[:-1]))
 
 
 def append(k_cache, v_cache, k_new, v_new, seqlens, *, block_table=None, block_size=0):
