@@ -15,6 +15,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Valid rows of a sequence: its length clamped to [0, Lmax], so a length
+// outside the documented range never sends a read or write past the
+// sequence's slice of the cache.
+__device__ __forceinline__ int valid_rows(int len, int Lmax) { return min(max(len, 0), Lmax); }
+
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16(
     const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
-    const int n = seqlens[b];
+    const int n = valid_rows(seqlens[b], Lmax);
     const int start = s * chunk;
     const int end = min(start + chunk, n);
     if (S > 1 && start >= end) return;  // empty split: the merge skips it
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16_tiles(
     const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
-    const int n = seqlens[b];
+    const int n = valid_rows(seqlens[b], Lmax);
     const int start = s * chunk;
     const int end = min(start + chunk, n);
     if (S > 1 && start >= end) return;  // empty split: the merge skips it
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
     const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
-    const int n = seqlens[b];
+    const int n = valid_rows(seqlens[b], Lmax);
     const int start = s * chunk;
     const int end = min(start + chunk, n);
     if (S > 1 && start >= end) return;
@@ -659,10 +659,11 @@ template <int D, bool BF16OUT>
 __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws_acc,
                                                    const float* __restrict__ ws_ml,
                                                    const int32_t* __restrict__ seqlens, int Hq,
-                                                   int S, int chunk, void* __restrict__ out) {
+                                                   int Lmax, int S, int chunk,
+                                                   void* __restrict__ out) {
     constexpr int PER = D / 64;
     const int64_t row = blockIdx.x;
-    const int n = seqlens[row / Hq];
+    const int n = valid_rows(seqlens[row / Hq], Lmax);
     float acc[PER];
     const float L = merge_split_row<D>(ws_acc, ws_ml, n, row, S, [&](int len, int& s0, int& se) {
         s0 = 0;

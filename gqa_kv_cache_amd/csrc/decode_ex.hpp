@@ -20,6 +20,11 @@
 //     is a bf16 value) when K is staged in LDS and when the V fragments are built.  The
 //     per-KV-head scales never touch the elements: k_scale multiplies the
 //     score factor and v_scale the output.
+//   - The append of the T new rows (Algorithm 2 of "GQA reading notes" stores
+//     the new K/V before attending) happens in the same launch: rows at or
+//     past n - T are read from k_new/v_new instead of the cache, and the
+//     workgroup whose piece holds such a row stores it into the cache.  No
+//     workgroup reads a cache row that another one writes in the same call.
 // Splits write (m, l, acc) like the plain kernel; decode_ex_merge combines
 // the splits that intersect the keys any token of the sequence can see.
 #pragma once
@@ -108,6 +113,35 @@ __device__ __forceinline__ void ex_load_step(ExStepData<D, KV8>& st, const __amd
                 st.vB[t][r] = ex_load_v<D, KV8>(vr[t], vv, r * rs);
             else
                 st.vB[t][r] = ex_load_v<D, KV8>(vr[0], vv, (16 * t + r) * rs);
+        }
+}
+
+// The rows of a step at or past `nw` (the first appended row) come from the
+// new rows [B,T,Hkv,d] instead of the cache, whose resource ends before them
+// and so returned zeros there: OR the new rows in.  Rows at or past `end`
+// stay zero.  kn/vn point at new row (b, 0, g).
+template <int D, bool KV8>
+__device__ __forceinline__ void ex_merge_new_rows(ExStepData<D, KV8>& st, const uint8_t* kn,
+                                                  const uint8_t* vn, int key0, int nw, int end,
+                                                  int T, int rs, int lane) {
+    typedef ExShape<D, KV8> Sh;
+    typedef typename ExVRaw<D, KV8>::T VR;
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Sh::KLD; ++i) {
+        const int row = key0 + Sh::RPI * i + lane / Sh::CPR;
+        const int t = row - nw;
+        if (t >= 0 && t < T && row < end)
+            st.kR[i] |= *reinterpret_cast<const u32x4*>(kn + (int64_t)t * rs + 16 * (lane % Sh::CPR));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = key0 + 16 * h + 4 * grp + r;
+            const int t = row - nw;
+            if (t >= 0 && t < T && row < end)
+                st.vB[h][r] |= *reinterpret_cast<const VR*>(vn + (int64_t)t * rs + Sh::VB * col);
         }
 }
 
@@ -244,12 +278,12 @@ __device__ __forceinline__ int ex_first_key(int n, int T, int window) {
 // ---------------------------------------------------------------------------
 template <int D, int NT, int KV, int NWV, bool H16>
 __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const uint16_t* __restrict__ q, uint8_t* kc, uint8_t* vc,
     const int32_t* __restrict__ seqlens, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
-    int bs, int T, int Hq, int Hkv, int Lmax, int gsize, int S, int chunk, int window,
-    float c_log2, uint16_t* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml) {
+    int bs, int num_blocks, const uint8_t* k_new, const uint8_t* v_new, int T, int Hq, int Hkv,
+    int Lmax, int gsize, int S, int chunk, int window, float c_log2, uint16_t* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
     constexpr bool KV8 = KV != 0;  // one-byte FP8 rows (KV: 1 = E4M3, 2 = E5M2)
     typedef DecodeShape<D> Sh;
     typedef ExShape<D, KV8> Ex;
@@ -272,13 +306,41 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     const int bg = blockIdx.x % nbg;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
-    const int n = seqlens[b];
+    const int n_in = seqlens[b];
+    const int n = valid_rows(n_in, Lmax);
     const int first = ex_first_key(n, T, window);
     const int start = s * chunk;
     const int end = min(start + chunk, n);
     if (max(start, first) >= end) return;  // no token sees this split: the merge skips it
 
     const int rs = Hkv * Ex::ROWB;  // bytes between consecutive rows of one KV head
+    // First row that comes from the new rows (none without an append).
+    const int nw = k_new ? n_in - T : INT_MAX;
+    const uint8_t* kn = k_new ? k_new + (((int64_t)b * T) * Hkv + g) * Ex::ROWB : nullptr;
+    const uint8_t* vn = v_new ? v_new + (((int64_t)b * T) * Hkv + g) * Ex::ROWB : nullptr;
+    // Cache row j of this sequence and KV head; nullptr for a block id
+    // outside the pool (never dereferenced then).
+    auto cache_row = [&](uint8_t* base, int j) __attribute__((always_inline)) -> uint8_t* {
+        if (!block_table) return base + (((int64_t)b * Lmax + j) * Hkv + g) * Ex::ROWB;
+        const int blk = block_table[(int64_t)b * max_blocks + j / bs];
+        if ((unsigned)blk >= (unsigned)num_blocks) return nullptr;
+        return base + (((int64_t)blk * bs + j % bs) * Hkv + g) * Ex::ROWB;
+    };
+    if (k_new) {
+        // Store the new rows of this piece: rows [nw, nw + T) inside
+        // [start, start + chunk) and inside the cache.
+        const int j0 = max(max(start, nw), 0);
+        const int j1 = min(min(start + chunk, nw + T), Lmax);
+        for (int it = threadIdx.x; it < (j1 - j0) * Ex::CPR; it += 64 * NWV) {
+            const int j = j0 + it / Ex::CPR;
+            const int c = 16 * (it % Ex::CPR);
+            uint8_t* kd = cache_row(kc, j);
+            uint8_t* vd = cache_row(vc, j);
+            if (!kd) continue;
+            *reinterpret_cast<u32x4*>(kd + c) = *reinterpret_cast<const u32x4*>(kn + (int64_t)(j - nw) * rs + c);
+            *reinterpret_cast<u32x4*>(vd + c) = *reinterpret_cast<const u32x4*>(vn + (int64_t)(j - nw) * rs + c);
+        }
+    }
     const int R = T * gsize;        // query rows of the workgroup
     const int h0 = g * gsize;
     u32x4* kt = k_tiles[wave];
@@ -318,40 +380,46 @@ __global__ __launch_bounds__(64 * NWV) void decode_ex_kernel(
     // to the valid rows (a resource of size 0 reads zeros only).  A step lies
     // in one block when the blocks hold a multiple of 32 rows; with 16-row
     // multiples (H16) each 16-row half gets its own resource, in its block.
+    // Rows the cache serves: below the split end and below the first new row.
+    const int cache_end = min(end, nw);
     auto load = [&](int key0, ExStepData<D, KV8>& st) __attribute__((always_inline)) {
         __amdgpu_buffer_rsrc_t kr[2], vr[2];
         if constexpr (H16) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int row0 = key0 + 16 * x;
-                const int valid = min(end - row0, 16);
+                const int valid = min(cache_end - row0, 16);
                 int nbytes = 0;
                 int64_t off = 0;
                 if (valid > 0) {
-                    nbytes = (valid - 1) * rs + Ex::ROWB;
-                    const int64_t blk = block_table[(int64_t)b * max_blocks + row0 / bs];
-                    off = ((blk * bs + row0 % bs) * Hkv + g) * Ex::ROWB;
+                    const int blk = block_table[(int64_t)b * max_blocks + row0 / bs];
+                    if ((unsigned)blk < (unsigned)num_blocks) {
+                        nbytes = (valid - 1) * rs + Ex::ROWB;
+                        off = (((int64_t)blk * bs + row0 % bs) * Hkv + g) * Ex::ROWB;
+                    }
                 }
                 kr[x] = make_rsrc(kc + off, nbytes);
                 vr[x] = make_rsrc(vc + off, nbytes);
             }
         } else {
             const uint8_t *kp, *vp;
+            const int valid = min(cache_end - key0, kDecodeStep);
+            int nbytes = valid > 0 ? (valid - 1) * rs + Ex::ROWB : 0;
             if (block_table) {
-                const int64_t blk = block_table[(int64_t)b * max_blocks + key0 / bs];
-                const int64_t off = ((blk * bs + key0 % bs) * Hkv + g) * Ex::ROWB;
+                const int blk = block_table[(int64_t)b * max_blocks + key0 / bs];
+                if ((unsigned)blk >= (unsigned)num_blocks) nbytes = 0;
+                const int64_t off = nbytes ? (((int64_t)blk * bs + key0 % bs) * Hkv + g) * Ex::ROWB : 0;
                 kp = kc + off;
                 vp = vc + off;
             } else {
                 kp = kseq + (int64_t)key0 * rs;
                 vp = vseq + (int64_t)key0 * rs;
             }
-            const int valid = min(end - key0, kDecodeStep);
-            const int nbytes = (valid - 1) * rs + Ex::ROWB;
             kr[0] = kr[1] = make_rsrc(kp, nbytes);
             vr[0] = vr[1] = make_rsrc(vp, nbytes);
         }
         ex_load_step<D, KV8, H16>(st, kr, vr, rs, lane);
+        if (key0 + kDecodeStep > nw) ex_merge_new_rows<D, KV8>(st, kn, vn, key0, nw, end, T, rs, lane);
     };
     constexpr int stride = NWV * kDecodeStep;
     if constexpr (KV8) {
@@ -453,11 +521,11 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_ex_merge(const float* __restrict__ ws_acc,
                                                       const float* __restrict__ ws_ml,
                                                       const int32_t* __restrict__ seqlens, int T,
-                                                      int Hq, int S, int chunk, int window,
+                                                      int Hq, int Lmax, int S, int chunk, int window,
                                                       uint16_t* __restrict__ out) {
     constexpr int PER = D / 64;
     const int64_t row = blockIdx.x;
-    const int n = seqlens[row / ((int64_t)T * Hq)];
+    const int n = valid_rows(seqlens[row / ((int64_t)T * Hq)], Lmax);
     float acc[PER];
     const float L = merge_split_row<D>(ws_acc, ws_ml, n, row, S, [&](int len, int& s0, int& se) {
         s0 = ex_first_key(len, T, window) / chunk;
@@ -469,35 +537,6 @@ __global__ __launch_bounds__(64) void decode_ex_merge(const float* __restrict__ 
         *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2_rne(L > 0.f ? acc[0] / L : 0.f, L > 0.f ? acc[PER - 1] / L : 0.f);
     else
         dst[0] = (uint16_t)f32_to_bf16_rne(L > 0.f ? acc[0] / L : 0.f);
-}
-
-// Append: row t of k_new/v_new [B,T,Hkv,d] (ROWB bytes per KV head) goes to
-// cache row seqlens[b] - T + t, contiguous or paged.  One workgroup per
-// (b, t, g); lanes copy 16-byte pieces.
-template <int ROWB>
-__global__ __launch_bounds__(64) void append_rows(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-                                                  const uint8_t* __restrict__ k_new,
-                                                  const uint8_t* __restrict__ v_new,
-                                                  const int32_t* __restrict__ seqlens,
-                                                  const int32_t* __restrict__ block_table,
-                                                  int max_blocks, int bs, int T, int Hkv, int Lmax) {
-    constexpr int PIECES = ROWB / 16;
-    const int g = blockIdx.x % Hkv;
-    const int bt = blockIdx.x / Hkv;
-    const int b = bt / T, t = bt % T;
-    const int j = seqlens[b] - T + t;
-    int64_t dst;
-    if (block_table) {
-        const int64_t blk = block_table[(int64_t)b * max_blocks + j / bs];
-        dst = ((blk * bs + j % bs) * Hkv + g) * ROWB;
-    } else {
-        dst = (((int64_t)b * Lmax + j) * Hkv + g) * ROWB;
-    }
-    const int64_t src = ((int64_t)bt * Hkv + g) * ROWB;
-    for (int p = threadIdx.x; p < PIECES; p += 64) {
-        *reinterpret_cast<u32x4*>(kc + dst + 16 * p) = *reinterpret_cast<const u32x4*>(k_new + src + 16 * p);
-        *reinterpret_cast<u32x4*>(vc + dst + 16 * p) = *reinterpret_cast<const u32x4*>(v_new + src + 16 * p);
-    }
 }
 
 }  // namespace gqa

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <climits>
 #include <cstdint>
+#include <cstdlib>
 
 #include "gqa.h"
 #include "common.hpp"
@@ -42,6 +43,49 @@ gqa_status current_cu_count(int* cus) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ----- debug check of the device-side lengths (GQA_CHECK_SEQLENS=1) ---------
+
+bool check_lengths_requested() {
+    const char* e = std::getenv("GQA_CHECK_SEQLENS");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+// Copies seqlens (and, with a block table, the table entries of every row a
+// sequence holds) to the host on the caller's stream, waits for them and
+// checks lo <= seqlens[b] <= Lmax and 0 <= entry < num_blocks.  Goes through
+// a fixed buffer on the stack, so it allocates nothing.  Skipped while the
+// stream is being captured into a graph, where nothing may wait.
+gqa_status check_lengths(hipStream_t hs, const int32_t* seqlens, int B, int lo, int Lmax,
+                         const int32_t* block_table, int max_blocks, int block_size,
+                         int num_blocks) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return GQA_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return GQA_OK;
+    constexpr int kBuf = 1024;
+    int32_t len[kBuf], ent[kBuf];
+    for (int b0 = 0; b0 < B; b0 += kBuf) {
+        const int nb = B - b0 < kBuf ? B - b0 : kBuf;
+        if (hipMemcpyAsync(len, seqlens + b0, sizeof(int32_t) * nb, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+            hipStreamSynchronize(hs) != hipSuccess)
+            return GQA_ERR_HIP;
+        for (int i = 0; i < nb; ++i) {
+            if (len[i] < lo || len[i] > Lmax) return GQA_ERR_SHAPE;
+            if (!block_table) continue;
+            const int used = (len[i] + block_size - 1) / block_size;  // blocks holding rows < len
+            const int32_t* row = block_table + (int64_t)(b0 + i) * max_blocks;
+            for (int e0 = 0; e0 < used; e0 += kBuf) {
+                const int ne = used - e0 < kBuf ? used - e0 : kBuf;
+                if (hipMemcpyAsync(ent, row + e0, sizeof(int32_t) * ne, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+                    hipStreamSynchronize(hs) != hipSuccess)
+                    return GQA_ERR_HIP;
+                for (int k = 0; k < ne; ++k)
+                    if (ent[k] < 0 || ent[k] >= num_blocks) return GQA_ERR_SHAPE;
+            }
+        }
+    }
+    return GQA_OK;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -183,12 +227,15 @@ void launch_decode_ex(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex_arg
                       float c, float* wa, float* wm) {
     dim3 block;
     auto q = static_cast<const uint16_t*>(a->q);
-    auto k = static_cast<const uint8_t*>(a->k_cache);
-    auto v = static_cast<const uint8_t*>(a->v_cache);
+    auto k = static_cast<uint8_t*>(a->k_cache);
+    auto v = static_cast<uint8_t*>(a->v_cache);
+    auto kn = static_cast<const uint8_t*>(a->k_new);
+    auto vn = static_cast<const uint8_t*>(a->v_new);
     auto o = static_cast<uint16_t*>(a->out);
     const int gs = a->Hq / a->Hkv;
 #define GQA_EX_ARGS q, k, v, a->seqlens, a->k_scale, a->v_scale, a->block_table, a->max_blocks, \
-                    a->block_size, a->T, a->Hq, a->Hkv, a->Lmax, gs, p.splits, p.chunk, a->window, c, o, wa, wm
+                    a->block_size, a->num_blocks, kn, vn, a->T, a->Hq, a->Hkv, a->Lmax, gs, p.splits, \
+                    p.chunk, a->window, c, o, wa, wm
 #define GQA_EX_CASE(N) block = dim3(64 * ex_waves<KV != 0, N>()); \
     hipLaunchKernelGGL((gqa::decode_ex_kernel<D, N, KV, ex_waves<KV != 0, N>(), H16>), grid, block, 0, hs, GQA_EX_ARGS)
     switch (nt) {
@@ -217,15 +264,6 @@ void launch_decode_ex_for(int nt, dim3 grid, hipStream_t hs, const gqa_decode_ex
         if (h16) launch_decode_ex<D, 0, true>(nt, grid, hs, a, p, c, wa, wm);
         else launch_decode_ex<D, 0, false>(nt, grid, hs, a, p, c, wa, wm);
     }
-}
-
-template <int ROWB>
-void launch_append(hipStream_t hs, const gqa_decode_ex_args* a) {
-    dim3 grid((unsigned)((int64_t)a->B * a->T * a->Hkv));
-    hipLaunchKernelGGL((gqa::append_rows<ROWB>), grid, dim3(64), 0, hs,
-                       static_cast<uint8_t*>(a->k_cache), static_cast<uint8_t*>(a->v_cache),
-                       static_cast<const uint8_t*>(a->k_new), static_cast<const uint8_t*>(a->v_new),
-                       a->seqlens, a->block_table, a->max_blocks, a->block_size, a->T, a->Hkv, a->Lmax);
 }
 
 gqa_status validate_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -368,6 +406,10 @@ gqa_status run_decode(const void* q, const void* k_cache, const void* v_cache,
                       gqa_dtype dtype, void* out, void* workspace, const DecodePlan& plan,
                       void* stream) {
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (check_lengths_requested()) {
+        const gqa_status st = check_lengths(hs, seqlens, B, 0, Lmax, nullptr, 0, 1, 0);
+        if (st != GQA_OK) return st;
+    }
     const int gs = Hq / Hkv;
     const int S = plan.splits;
     const float c = scale * gqa::kLog2e;
@@ -405,14 +447,14 @@ gqa_status run_decode(const void* q, const void* k_cache, const void* v_cache,
         dim3 mblock(64);
         if (dtype == GQA_BF16) {
             if (d == 128)
-                hipLaunchKernelGGL((gqa::decode_merge<128, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+                hipLaunchKernelGGL((gqa::decode_merge<128, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, Lmax, S, plan.chunk, out);
             else
-                hipLaunchKernelGGL((gqa::decode_merge<64, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+                hipLaunchKernelGGL((gqa::decode_merge<64, true>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, Lmax, S, plan.chunk, out);
         } else {
             if (d == 128)
-                hipLaunchKernelGGL((gqa::decode_merge<128, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+                hipLaunchKernelGGL((gqa::decode_merge<128, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, Lmax, S, plan.chunk, out);
             else
-                hipLaunchKernelGGL((gqa::decode_merge<64, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, S, plan.chunk, out);
+                hipLaunchKernelGGL((gqa::decode_merge<64, false>), mgrid, mblock, 0, hs, ws_acc, ws_ml, seqlens, Hq, Lmax, S, plan.chunk, out);
         }
         if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     }
@@ -451,18 +493,16 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
         return GQA_ERR_WORKSPACE;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (check_lengths_requested()) {
+        st = check_lengths(hs, a->seqlens, a->B, a->T, a->Lmax, a->block_table, a->max_blocks,
+                           a->block_size, a->num_blocks);
+        if (st != GQA_OK) return st;
+    }
     const int S = plan.splits;
     const int64_t rows = (int64_t)a->B * a->T * a->Hq;
     float* ws_acc = plan.ws_bytes ? static_cast<float*>(a->workspace) : nullptr;
     float* ws_ml = plan.ws_bytes ? ws_acc + rows * S * a->d : nullptr;
     (void)hipGetLastError();
-    if (a->k_new) {
-        const int rowb = a->d * plan.elt;
-        if (rowb == 256) launch_append<256>(hs, a);
-        else if (rowb == 128) launch_append<128>(hs, a);
-        else launch_append<64>(hs, a);
-        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
-    }
     const int nt = (a->T * (a->Hq / a->Hkv) + 15) / 16;
     const float c = a->scale * gqa::kLog2e;
     dim3 grid((unsigned)((int64_t)a->B * a->Hkv * S));
@@ -473,9 +513,9 @@ gqa_status gqa_decode_ex(const gqa_decode_ex_args* a, void* stream) {
         dim3 mgrid((unsigned)rows);
         auto o = static_cast<uint16_t*>(a->out);
         if (a->d == 128)
-            hipLaunchKernelGGL((gqa::decode_ex_merge<128>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, S, plan.chunk, a->window, o);
+            hipLaunchKernelGGL((gqa::decode_ex_merge<128>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, a->Lmax, S, plan.chunk, a->window, o);
         else
-            hipLaunchKernelGGL((gqa::decode_ex_merge<64>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, S, plan.chunk, a->window, o);
+            hipLaunchKernelGGL((gqa::decode_ex_merge<64>), mgrid, dim3(64), 0, hs, ws_acc, ws_ml, a->seqlens, a->T, a->Hq, a->Lmax, S, plan.chunk, a->window, o);
         if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
     }
     return GQA_OK;

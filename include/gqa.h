@@ -29,6 +29,16 @@
  *     products are formed exactly in fp32 by the matrix cores); bf16 outputs
  *     are rounded to nearest-even.  Results are deterministic run to run.
  *   - Calls are reentrant and thread-safe.  `out` must not alias an input.
+ *   - Lengths live in device memory and are not checked on the host by
+ *     default.  A kernel clamps a length to [0, Lmax] (and skips block-table
+ *     entries outside the pool), so a value outside its documented range
+ *     never sends a read or write past the caller's buffers; the results of
+ *     that sequence are then unspecified.  With the environment variable
+ *     GQA_CHECK_SEQLENS=1, the decode calls first copy seqlens (and the
+ *     block-table entries of every row a sequence holds) to the host on
+ *     `stream`, wait for them, and return GQA_ERR_SHAPE before any launch if
+ *     one is out of range.  This debug check synchronises the stream; it is
+ *     skipped while the stream is being captured into a graph.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -80,8 +90,8 @@ const char *gqa_status_str(gqa_status s);
  *   k_cache  [B, Lmax, Hkv, d]   rows j >= seqlens[b] are never read
  *   v_cache  [B, Lmax, Hkv, d]
  *   seqlens  [B] int32, DEVICE memory; precondition 0 <= seqlens[b] <= Lmax
- *            (not checked: it lives on the device).  seqlens[b] == 0 gives
- *            out[b,:,:] = 0.
+ *            (checked only under GQA_CHECK_SEQLENS=1, see the conventions
+ *            above).  seqlens[b] == 0 gives out[b,:,:] = 0.
  *   out      [B, Hq, d]
  *   scale    softmax scale, normally 1/sqrt(d)
  *   dtype    GQA_F32 or GQA_BF16
@@ -196,15 +206,20 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int P
  *            block_table[b * max_blocks + j / block_size].  Written when
  *            k_new is given; read otherwise.
  *   seqlens  [B] int32: valid rows per sequence AFTER the append.
- *            Precondition (not checked, device data): T <= seqlens[b] <= Lmax.
+ *            Precondition: T <= seqlens[b] <= Lmax (checked only under
+ *            GQA_CHECK_SEQLENS=1, see the conventions above).
  *   block_table  [B, max_blocks] int32 or NULL.  block_size must be a multiple
  *            of 16; Lmax must equal max_blocks * block_size.  Precondition:
- *            every entry used is in [0, num_blocks).
+ *            every entry used is in [0, num_blocks) (entries outside are
+ *            never followed: their rows read as zeros and take no append).
  *   k_scale, v_scale  [Hkv] fp32, the FP8 formats only (required there,
  *            ignored for bf16): K row values are fp8(byte) * k_scale[g], V
  *            likewise with v_scale[g], fp8() the value the format encodes.
  *   k_new, v_new  [B, T, Hkv, d] in kv_dtype, or both NULL.  When given they
- *            are first stored, byte for byte, at rows seqlens[b] - T + t.
+ *            are stored, byte for byte, at rows seqlens[b] - T + t, in the
+ *            same launch that attends: the attention reads those rows from
+ *            k_new/v_new, never from the cache, so their cache contents
+ *            before the call do not matter.  They must not overlap the cache.
  *   window   0 = every key; W > 0 = the last W keys of each token.
  *   T * (Hq/Hkv) <= 64; d 64 or 128; B, T, Hq, Hkv, Lmax >= 1;
  *            32 * Hkv * d * (bytes per cache element) <= 2^31 - 1 (the rows of

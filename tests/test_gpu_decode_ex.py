@@ -3,7 +3,9 @@
 Covers several new tokens per sequence, the append of their K/V rows, FP8
 (E4M3 and E5M2) caches with per-KV-head scales, paged caches and sliding windows, alone
 and combined, with forced and automatic splits.  Tolerance (bf16 q and out,
-fp32 accumulation): |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise.
+fp32 accumulation): |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise, and
+every element inside the bound derived from the kernel's arithmetic
+(tests/bounds.py).
 Cache rows past each length, pool blocks no sequence uses and the rows of the
 new tokens before the append hold NaN, so a stray read would show.
 """
@@ -14,6 +16,7 @@ import torch
 import gqa_inputs as gi
 import gqa_kv_cache_amd as gqa
 from oracle import reference as orc
+from tests import bounds as bd
 from tests.gpu_util import from_dev, to_dev
 from tests.helpers import bf16_tol_ok
 
@@ -61,6 +64,15 @@ def check(c, got, ref):
     return err
 
 
+def check_oracle(c, got, rows=None):
+    """Stated tolerance and derived bound against the oracle (all rows, or
+    the flat ((b*T + t)*Hq + h) rows given)."""
+    ref, sig, mu, kap, n = bd.ex_terms(c, rows)
+    err = check(c, got, ref)
+    bd.assert_within(got, ref, bd.decode_bound(ref, sig, mu, kap, n, c.q.shape[-1]), c.name)
+    return err
+
+
 def case(B=3, T=2, Hq=16, Hkv=4, d=128, Lmax=256, seqlens=(256, 97, 5), kv="same", paged=False,
          block_size=64, window=0, seed=40):
     name = "ex_B%d_T%d_Hq%d_Hkv%d_d%d_L%d_%s%s_w%d" % (B, T, Hq, Hkv, d, Lmax, kv,
@@ -75,7 +87,7 @@ def case(B=3, T=2, Hq=16, Hkv=4, d=128, Lmax=256, seqlens=(256, 97, 5), kv="same
 def test_tokens_and_groups(d, T, Hq, Hkv):
     c = case(T=T, Hq=Hq, Hkv=Hkv, d=d, seqlens=(256, 97, max(T, 5)), seed=41)
     out, _, _ = run_ex(c)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("kv", ["same", "fp8", "e5m2"])
@@ -83,7 +95,7 @@ def test_tokens_and_groups(d, T, Hq, Hkv):
 def test_splits(kv, splits):
     c = case(kv=kv, T=3, seqlens=(256, 200, 33), seed=42)
     out, _, _ = run_ex(c, num_splits=splits)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("kv", ["fp8", "e5m2"])
@@ -92,7 +104,7 @@ def test_splits(kv, splits):
 def test_fp8_cache(kv, d, T):
     c = case(kv=kv, d=d, T=T, Hq=32 if T == 8 else 16, seqlens=(256, 97, max(T, 5)), seed=43)
     out, _, _ = run_ex(c)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
@@ -121,14 +133,13 @@ def test_fp8_dtypes_name_their_format():
     """A float8_e5m2 (or float8_e4m3fn) cache needs no kv_format; a uint8 one
     is read as the kv_format it is given."""
     c = case(kv="e5m2", T=2, seed=53)
-    ref = oracle_ex(c)
     sl = torch.from_numpy(c.seqlens).cuda()
     ks, vs = torch.from_numpy(c.k_scale).cuda(), torch.from_numpy(c.v_scale).cuda()
     k = _dev_cache(c.k).view(torch.float8_e5m2)
     v = _dev_cache(c.v).view(torch.float8_e5m2)
     out = gqa.decode_ex(to_dev(c.q), k, v, sl, scale=c.scale, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
-    check(c, from_dev(out), ref)
+    check_oracle(c, from_dev(out))
     with pytest.raises(TypeError):
         gqa.decode_ex(to_dev(c.q), k, v, sl, scale=c.scale, k_scale=ks, v_scale=vs,
                       kv_format="e4m3")
@@ -146,7 +157,7 @@ def test_paged(kv, block_size, splits):
     Lmax = -(-256 // block_size) * block_size   # whole blocks (288 for 48-row blocks)
     c = case(kv=kv, paged=True, block_size=block_size, T=2, Lmax=Lmax, seed=44)
     out, _, _ = run_ex(c, num_splits=splits)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("window", [1, 5, 31, 32, 33, 100, 255, 4096])
@@ -154,7 +165,7 @@ def test_paged(kv, block_size, splits):
 def test_window(window, splits):
     c = case(window=window, T=3, seqlens=(256, 130, 7), seed=45)
     out, _, _ = run_ex(c, num_splits=splits)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("kv,block_size", [("fp8", 32), ("e5m2", 32), ("same", 16), ("fp8", 16)])
@@ -163,7 +174,7 @@ def test_everything_together(kv, block_size):
              seqlens=(256, 161, 64, 4), seed=46)
     for splits in (0, 1, 5):
         out, _, _ = run_ex(c, num_splits=splits)
-        check(c, from_dev(out), oracle_ex(c))
+        check_oracle(c, from_dev(out))
 
 
 @pytest.mark.parametrize("kv,paged,block_size", [("same", False, 64), ("same", True, 64),
@@ -180,13 +191,32 @@ def test_append_writes_cache_rows_exactly(kv, paged, block_size):
     got_v = v.view(torch.uint8).cpu().numpy().reshape(-1)
     assert np.array_equal(got_k, want_k.view(np.uint8).reshape(-1))
     assert np.array_equal(got_v, want_v.view(np.uint8).reshape(-1))
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
+
+
+@pytest.mark.parametrize("kv,paged,block_size", [("same", False, 64), ("fp8", True, 16),
+                                                 ("e5m2", True, 32), ("same", True, 48)])
+def test_append_rows_across_piece_boundaries(kv, paged, block_size):
+    """The new rows straddle piece and 32-key step boundaries (rows 62-65 and
+    126-129 with pieces of 32 or 64 keys): each piece stores and reads its own
+    share of them, in the one launch."""
+    Lmax = -(-256 // block_size) * block_size
+    c = case(B=3, T=4, Hq=16, Hkv=4, kv=kv, paged=paged, block_size=block_size, Lmax=Lmax,
+             seqlens=(66, 130, 4), seed=56)
+    for splits in (-(-Lmax // 64), -(-Lmax // 32)):
+        out, k, v = run_ex(c, append=True, num_splits=splits)
+        want_k, want_v = c.k_pre.copy(), c.v_pre.copy()
+        orc.append(want_k, want_v, c.k_new, c.v_new, c.seqlens, block_table=c.block_table,
+                   block_size=c.block_size)
+        assert np.array_equal(k.view(torch.uint8).cpu().numpy().reshape(-1), want_k.view(np.uint8).reshape(-1))
+        assert np.array_equal(v.view(torch.uint8).cpu().numpy().reshape(-1), want_v.view(np.uint8).reshape(-1))
+        check_oracle(c, from_dev(out))
 
 
 def test_without_append_reads_the_cache():
     c = case(T=2, seed=48)
     out, _, _ = run_ex(c, append=False)
-    check(c, from_dev(out), oracle_ex(c))
+    check_oracle(c, from_dev(out))
 
 
 def test_single_token_matches_plain_decode():
@@ -200,16 +230,13 @@ def test_single_token_matches_plain_decode():
 
 
 @pytest.mark.parametrize("kv", ["fp8", "e5m2"])
-def test_fp8_70b_layer_sampled(kv):
+def test_fp8_70b_layer_every_row(kv):
     """The 70B-class layer shape with an FP8 cache and 4 new tokens per sequence,
-    sampled rows against the oracle."""
+    every row against the oracle."""
     c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096] * 32, "bf16", seed=50, kv=kv,
                           invalid="zero", name="ex_%s_B32_T4_Hq64_Hkv8_d128_L4096" % kv)
     out, _, _ = run_ex(c)
-    rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))
-    got = from_dev(out).reshape(-1, 128)[rows]
-    check(c, got, oracle_ex(c, rows=rows))
+    check_oracle(c, from_dev(out))
 
 
 def test_run_twice_bitwise():
@@ -228,25 +255,22 @@ def test_paged16_halves_in_different_blocks(kv, d):
              paged=True, block_size=16, seed=54)
     for splits in (0, 1, 3):
         out, _, _ = run_ex(c, num_splits=splits)
-        check(c, from_dev(out), oracle_ex(c))
+        check_oracle(c, from_dev(out))
 
 
-def test_paged16_70b_layer_sampled():
+def test_paged16_70b_layer_every_row():
     """The 70B-class layer shape in a pool of 16-row blocks, 4 new tokens,
-    sampled rows against the oracle."""
+    every row against the oracle."""
     c = gi.decode_ex_case(32, 4, 64, 8, 128, 4096, [4096 - 7 * i for i in range(32)], "bf16",
                           seed=55, paged=True, block_size=16, invalid="zero",
                           name="ex_paged16_B32_T4_Hq64_Hkv8_d128_L4096")
     out, _, _ = run_ex(c)
-    rng = np.random.default_rng(8)
-    rows = np.sort(rng.choice(32 * 4 * 64, 96, replace=False))
-    got = from_dev(out).reshape(-1, 128)[rows]
-    check(c, got, oracle_ex(c, rows=rows))
+    check_oracle(c, from_dev(out))
 
 
 # The extended workloads the benchmark times (70B-class layer shape, seed 60,
 # zero beyond each length), in the same launch configuration (automatic
-# splits), on sampled rows.
+# splits), every row.
 L70 = dict(B=32, T=1, Hq=64, Hkv=8, d=128, Lmax=4096, seqlens=[4096] * 32, dtype="bf16",
            invalid="zero")
 
@@ -259,13 +283,9 @@ L70 = dict(B=32, T=1, Hq=64, Hkv=8, d=128, Lmax=4096, seqlens=[4096] * 32, dtype
     ("decode_ex_bf16_paged16_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=16)),
     ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),
 ])
-def test_benchmark_extended_workloads_sampled(name, extra):
+def test_benchmark_extended_workloads_every_row(name, extra):
     a = dict(L70)
     a.update(extra)
     c = gi.decode_ex_case(seed=60, name=name, **a)
     out, _, _ = run_ex(c, append=False)
-    T = c.q.shape[1]
-    rng = np.random.default_rng(9)
-    rows = np.sort(rng.choice(32 * T * 64, 64, replace=False))
-    got = from_dev(out).reshape(-1, 128)[rows]
-    check(c, got, oracle_ex(c, rows=rows))
+    check_oracle(c, from_dev(out))
