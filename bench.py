@@ -9,8 +9,11 @@ Infinity Cache or the L2.  Prints one JSON line.
 
 Also measured and reported in the same line: the causal prefill (B=2,
 P=4096, Hq=32, Hkv=8, d=128) against the bf16 matrix-core peak, the
-head-sharing sweep (B=16, Hq=64, d=128, L=2048, Hkv in 64/16/8/4/1), and the
-CPU oracle on the decode workload as a baseline.
+head-sharing sweep (B=16, Hq=64, d=128, L=2048, Hkv in 64/16/8/4/1), the
+ragged batch (B=64, Hq=32, Hkv=8, d=128, lengths U[1, 32768]), the tiny fp32
+step (B=1, Hq=8, d=64, L=128, Hkv 2/8/1), the extended decode steps (FP8,
+paged, window, several new tokens, and the append with the attention), and
+the fp64 CPU oracle timed on the host cores beside decode and prefill.
 """
 from __future__ import annotations
 
@@ -33,14 +36,16 @@ METRIC = "GQA decode: achieved HBM TB/s + µs/step, Hq=64 Hkv=8 d=128 B=32 L=409
 
 DECODE_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/decode.hpp",
                   "gqa_kv_cache_amd/csrc/gqa_api.hip")
-PREFILL_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/prefill.hpp",
-                   "gqa_kv_cache_amd/csrc/gqa_api.hip")
+PREFILL_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/prefill.hpp")
 EXT_SOURCES = ("gqa_kv_cache_amd/csrc/common.hpp", "gqa_kv_cache_amd/csrc/decode.hpp",
                "gqa_kv_cache_amd/csrc/decode_ex.hpp", "gqa_kv_cache_amd/csrc/gqa_api.hip")
 DECODE_PMC = "profiles/decode_bf16_B32_Hq64_Hkv8_d128_L4096.pmc.txt"
 EXT_FP8_PMC = {"e4m3": "profiles/decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096.pmc.txt",
                "e5m2": "profiles/decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096.pmc.txt"}
 PREFILL_PMC = "profiles/prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal.pmc.txt"
+PREFILL_MFMA = "profiles/prefill_bf16_B2_P4096_Hq32_Hkv8_d128_causal.mfma.txt"
+DECODE_TARGET_FRAC = 0.70      # of HBM bandwidth
+PREFILL_TARGET_FRAC = 0.50     # of the bf16 dense matrix peak
 
 
 def source_digest(paths) -> str:
@@ -53,13 +58,9 @@ def source_digest(paths) -> str:
     return h.hexdigest()
 
 
-def pmc_traffic(summary_rel, sources):
-    """HBM bytes per launch from a committed FETCH_SIZE/WRITE_SIZE summary.
-
-    The summary records the digest of the kernel sources it was measured on;
-    if those sources have changed since, the figure no longer applies and
-    None is returned.
-    """
+def profile_fields(summary_rel, sources):
+    """Fields of a committed rocprofv3 summary, or None if it is missing or was
+    measured on other kernel sources (the summary records their digest)."""
     path = os.path.join(ROOT, summary_rel)
     if not os.path.exists(path):
         return None
@@ -71,10 +72,34 @@ def pmc_traffic(summary_rel, sources):
                 vals[k.strip()] = v.strip()
     if vals.get("source_sha256") != source_digest(sources):
         return None
+    return vals
+
+
+def pmc_traffic(summary_rel, sources):
+    """HBM bytes per launch from a committed FETCH_SIZE/WRITE_SIZE summary
+    (None when the kernel sources have changed since it was taken)."""
+    vals = profile_fields(summary_rel, sources)
     try:
         return float(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (TypeError, KeyError, ValueError):
         return None
+
+
+def mfma_counters(summary_rel, sources):
+    """Matrix-core utilisation of the prefill kernel from its committed counter
+    summary: busy cycles over SIMD cycles, the shader clock over the launch,
+    and executed against algorithmic FLOP (None when the sources changed)."""
+    vals = profile_fields(summary_rel, sources)
+    if vals is None:
+        return None
+    out = {}
+    for k in ("mfma_busy_frac", "shader_clock_ghz", "executed_flop_per_launch",
+              "algorithmic_flop_per_launch", "useful_mfma_frac_at_measured_clock"):
+        try:
+            out[k] = float(vals[k])
+        except (KeyError, ValueError):
+            pass
+    return out or None
 
 
 def log(msg):
@@ -154,8 +179,9 @@ def bench_decode_case(case, steps, warmup, copies, torch, gqa):
     return res, out
 
 
-def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
-    """Time gqa_decode_ex (no append) over rotated cache copies; returns a result dict."""
+def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9, append=False):
+    """Time gqa_decode_ex over rotated cache copies, with the append of the
+    new rows in the same call when `append`; returns a result dict."""
     def dev(a):
         if a.dtype.name == "uint8":
             return torch.from_numpy(a).cuda()
@@ -178,6 +204,9 @@ def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
     if case.block_table is not None:
         kw["block_table"] = torch.from_numpy(case.block_table).cuda()
         kw["block_size"] = case.block_size
+    if append:
+        kw["k_new"] = dev(case.k_new)
+        kw["v_new"] = dev(case.v_new)
     out = torch.empty_like(q)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
 
@@ -192,10 +221,15 @@ def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
     # rows some token of the sequence can see, read once per KV head; q and out
     first = [max(0, int(n) - T - case.window + 1) if case.window > 0 else 0 for n in case.seqlens]
     rows = sum(int(n) - f for n, f in zip(case.seqlens, first))
+    # K/V rows read once per KV head (the new ones from k_new/v_new), the new
+    # rows stored once when appending, q read and out written once
     nbytes = rows * 2 * Hkv * d * elt + 2 * B * T * Hq * d * 2
+    if append:
+        nbytes += B * T * 2 * Hkv * d * elt
     us = ev_ms * 1e3
     del ks, vs
     return {"workload": case.name, "T": T, "kv_dtype": case.kv_format or "bf16",
+            "append": append,
             "paged_block_size": case.block_size or None, "window": case.window or None,
             "bytes": nbytes, "us_per_step": us, "us_per_call_median": median(per_call) * 1e3,
             "achieved_TBps": nbytes / (us * 1e-6) / 1e12,
@@ -203,39 +237,114 @@ def bench_decode_ex(case, steps, warmup, torch, gqa, min_total_bytes=1.0e9):
             "new_tokens_per_s": B * T / (us * 1e-6), "cache_copies_rotated": copies}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def time_oracle(fn, min_seconds, max_passes):
+    """Run fn() until min_seconds have passed (at least once); returns
+    (passes, total seconds, last result)."""
+    passes, total, res = 0, 0.0, None
+    while passes < max_passes and (passes == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        res = fn()
+        total += time.perf_counter() - t0
+        passes += 1
+    return passes, total, res
+
+
+def widen_out(t, torch):
+    import numpy as np
+    if t.dtype == torch.bfloat16:
+        return (t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32)
+                << np.uint32(16)).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
 def cpu_baseline(case, gpu_out, torch, min_seconds=10.0, max_passes=200):
-    """Time the fp64 oracle on the decode workload on the host cores."""
+    """Time the fp64 oracle on the decode workload on the host cores (all of
+    them), and once on one thread; compare the GPU output with it."""
     import numpy as np
     from oracle import counts, reference as orc
 
-    passes, total = 0, 0.0
-    ref = None
-    while passes < max_passes and (passes == 0 or total < min_seconds):
-        t0 = time.perf_counter()
-        ref = orc.decode(case.q, case.k, case.v, case.seqlens, case.scale)
-        total += time.perf_counter() - t0
-        passes += 1
+    passes, total, ref = time_oracle(
+        lambda: orc.decode(case.q, case.k, case.v, case.seqlens, case.scale), min_seconds, max_passes)
     B, Hq, d = case.q.shape
     Hkv = case.k.shape[2]
-    nbytes = counts.decode_bytes(case.seqlens, Hq, Hkv, d, 2) * passes
-    got = (gpu_out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32)
-           << np.uint32(16)).view(np.float32).astype(np.float64)
-    err = np.abs(got - ref)
+    step_bytes = counts.decode_bytes(case.seqlens, Hq, Hkv, d, 2)
+    err = np.abs(widen_out(gpu_out, torch) - ref)
     ok = bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))
+    cores = orc.num_threads()
+    prev = orc.set_threads(1)
+    try:
+        p1, t1, _ = time_oracle(
+            lambda: orc.decode(case.q, case.k, case.v, case.seqlens, case.scale), 0.0, 1)
+    finally:
+        orc.set_threads(prev)
     return {
-        "value": nbytes / total / 1e12, "unit": "TB/s", "cores": orc.num_threads(),
+        "value": step_bytes * passes / total / 1e12, "unit": "TB/s", "cores": cores,
         "kind": "oracle",
         "sample": "whole decode workload (all 32 sequences x 64 query heads x 4096 rows), "
                   "%d pass(es), fp64 C oracle with OpenMP, %.2f s" % (passes, total),
         "us_per_step": total / passes * 1e6,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
         "gpu_vs_oracle_max_abs_err": float(err.max()), "gpu_vs_oracle_within_tol": ok,
+        "single_thread": {"us_per_step": t1 / p1 * 1e6,
+                          "value": step_bytes * p1 / t1 / 1e12, "unit": "TB/s", "cores": 1},
     }
 
 
-def bench_prefill(steps, warmup, torch, gqa):
+def cpu_baseline_tiny(torch, min_seconds=1.0):
+    """The fp64 oracle on the tiny fp32 step (B1 Hq8 d64 L128, Hkv 2/8/1), all
+    host cores and one thread."""
     import gqa_inputs as gi
-    c = gi.prefill_causal()
+    from oracle import reference as orc
+
+    res = []
+    for hkv in (2, 8, 1):
+        c = gi.tiny_decode(hkv)
+        fn = lambda: orc.decode(c.q, c.k, c.v, c.seqlens, c.scale)  # noqa: E731
+        pa, ta, _ = time_oracle(fn, min_seconds, 100000)
+        prev = orc.set_threads(1)
+        try:
+            p1, t1, _ = time_oracle(fn, min_seconds, 100000)
+        finally:
+            orc.set_threads(prev)
+        res.append({"Hkv": hkv, "us_per_step_all_cores": ta / pa * 1e6,
+                    "us_per_step_single_thread": t1 / p1 * 1e6})
+    return res
+
+
+def cpu_baseline_prefill(case, gpu_out, torch):
+    """The fp64 oracle on the whole causal prefill workload, once, on the host
+    cores; the GPU output is compared with it."""
+    import numpy as np
+    from oracle import counts, reference as orc
+
+    t0 = time.perf_counter()
+    ref = orc.prefill(case.q, case.k, case.v, True, case.scale)
+    secs = time.perf_counter() - t0
+    B, P, Hq, d = case.q.shape
+    flops = counts.prefill_flops(B, P, Hq, d, True)
+    err = np.abs(widen_out(gpu_out, torch) - ref)
+    return {
+        "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+        "sample": "whole causal prefill workload (2 x 4096 positions x 32 query heads), one pass, "
+                  "fp64 C oracle with OpenMP, %.2f s" % secs,
+        "us_per_step": secs * 1e6, "cpu": cpu_model(),
+        "gpu_vs_oracle_max_abs_err": float(err.max()),
+        "gpu_vs_oracle_within_tol": bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref))),
+    }
+
+
+def bench_prefill(steps, warmup, torch, gqa, c):
     q, k, v = to_dev(c.q, torch), to_dev(c.k, torch), to_dev(c.v, torch)
     out = torch.empty_like(q)
 
@@ -254,9 +363,28 @@ def bench_prefill(steps, warmup, torch, gqa):
         "us_per_step_stream": ev_ms * 1e3,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                     "target_frac": PREFILL_TARGET_FRAC,
+                     "target_met": tflops / BF16_PEAK_TFLOPS >= PREFILL_TARGET_FRAC,
                      "traffic": pmc_traffic(PREFILL_PMC, PREFILL_SOURCES),
+                     "mfma_counters": mfma_counters(PREFILL_MFMA, PREFILL_SOURCES),
                      "kernel": "prefill_bf16"},
-    }
+    }, out
+
+
+def bench_tiny(steps, warmup, torch, gqa):
+    """The tiny fp32 step (B1 Hq8 d64 L128) for Hkv 2 (GQA), 8 (MHA), 1 (MQA):
+    launch-bound, reported for completeness."""
+    import gqa_inputs as gi
+    res = []
+    for hkv in (2, 8, 1):
+        c = gi.tiny_decode(hkv, invalid="zero")
+        r, o = bench_decode_case(c, steps, warmup, 1, torch, gqa)
+        res.append({"workload": c.name, "Hkv": hkv, "bytes": r["bytes"], "splits": r["splits"],
+                    "us_per_call_median": r["call_ms_median"] * 1e3,
+                    "us_per_step_stream": r["event_ms"] * 1e3,
+                    "time_at_hbm_peak_us": r["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6})
+        del o
+    return res
 
 
 def main():
@@ -268,9 +396,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--ragged", action="store_true", help="also time the ragged batch (8 GiB cache)")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch (8 GiB cache)")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 step")
     ap.add_argument("--no-extended", action="store_true",
-                    help="skip the extended decode (FP8, several tokens, paged, window)")
+                    help="skip the extended decode (FP8, several tokens, paged, window, append)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -318,19 +447,30 @@ def main():
                    "us_per_call_p90": res["call_ms_p90"] * 1e3,
                    "us_per_step_wall": res["wall_ms"] * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
+                     "frac": achieved / HBM_PEAK_GBS, "target_frac": DECODE_TARGET_FRAC,
+                     "target_met": achieved / HBM_PEAK_GBS >= DECODE_TARGET_FRAC,
                      "traffic": pmc_traffic(DECODE_PMC, DECODE_SOURCES),
                      "kernel": "decode_split_bf16" if res["splits"] == 1
                                else "decode_split_bf16 + decode_merge",
                      "launches_per_step": 1 if res["splits"] == 1 else 2},
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the decode workload")
+        log("timing the CPU oracle on the decode workload (all cores, then one thread)")
         line["cpu_baseline"] = cpu_baseline(case, out, torch)
-    del out
+        line["cpu_baseline"]["tiny_fp32"] = cpu_baseline_tiny(torch)
+    del out, case
+    if not args.no_tiny:
+        log("timing the tiny fp32 step")
+        line["tiny"] = bench_tiny(max(20, args.steps // 2), args.warmup, torch, gqa)
     if not args.no_prefill:
         log("timing prefill")
-        line["prefill"] = bench_prefill(max(10, args.steps // 4), max(3, args.warmup // 4), torch, gqa)
+        pc = gi.prefill_causal()
+        line["prefill"], pout = bench_prefill(max(10, args.steps // 4), max(3, args.warmup // 4),
+                                              torch, gqa, pc)
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on the whole prefill workload")
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pc, pout, torch)
+        del pout, pc
     if not args.no_sweep:
         sweep = []
         for hkv in gi.SWEEP_HKV:
@@ -340,13 +480,16 @@ def main():
             copies = max(2, min(8, math.ceil(1.0e9 / kv_bytes)))
             r, o = bench_decode_case(c, max(20, args.steps // 2), args.warmup, copies, torch, gqa)
             us = r["call_ms_mean"] * 1e3
-            fl_alu_us = r["flops"] / 78.6e12 * 1e6
+            # The scores and the weighted sum run on the bf16 matrix cores, so
+            # the arithmetic bound is the matrix peak; every setting sits far
+            # below its ridge (2516.6 / 8 = 315 FLOP per byte): HBM-bound.
             sweep.append({"Hkv": hkv, "bytes": r["bytes"], "flops": r["flops"], "splits": r["splits"],
                           "us_per_call_mean": us, "us_per_call_median": r["call_ms_median"] * 1e3,
                           "achieved_TBps": r["bytes"] / (us * 1e-6) / 1e12,
                           "hbm_frac": r["bytes"] / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                          "bound": "hbm", "flop_per_byte": r["flops"] / r["bytes"],
                           "time_at_hbm_peak_us": r["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6,
-                          "fp32_vector_alu_time_us": fl_alu_us})
+                          "time_at_bf16_mfma_peak_us": r["flops"] / (BF16_PEAK_TFLOPS * 1e12) * 1e6})
             del o
         line["sweep"] = sweep
     if not args.no_extended:
@@ -354,35 +497,40 @@ def main():
         L70 = dict(B=32, T=1, Hq=64, Hkv=8, d=128, Lmax=4096, seqlens=[4096] * 32, dtype="bf16",
                    invalid="zero")
         variants = [
-            ("decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096", dict(kv="fp8")),
-            ("decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096", dict(kv="e5m2")),
-            ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4)),
-            ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64)),
-            ("decode_ex_bf16_paged16_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=16)),
-            ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024)),
+            ("decode_ex_e4m3_B32_Hq64_Hkv8_d128_L4096", dict(kv="fp8"), False),
+            ("decode_ex_e5m2_B32_Hq64_Hkv8_d128_L4096", dict(kv="e5m2"), False),
+            ("decode_ex_bf16_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4), False),
+            ("decode_ex_bf16_paged64_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=64), False),
+            ("decode_ex_bf16_paged16_B32_Hq64_Hkv8_d128_L4096", dict(paged=True, block_size=16), False),
+            ("decode_ex_bf16_window1024_B32_Hq64_Hkv8_d128_L4096", dict(window=1024), False),
+            # the decode step of Algorithm 2 whole: append the new K/V rows, then attend
+            ("decode_ex_bf16_append_T1_B32_Hq64_Hkv8_d128_L4096", dict(T=1), True),
+            ("decode_ex_bf16_append_T4_B32_Hq64_Hkv8_d128_L4096", dict(T=4), True),
         ]
-        for name, extra in variants:
+        for name, extra, append in variants:
             log("timing %s" % name)
             a = dict(L70)
             a.update(extra)
             c = gi.decode_ex_case(seed=60, name=name, **a)
-            r = bench_decode_ex(c, max(20, args.steps // 2), args.warmup, torch, gqa)
+            r = bench_decode_ex(c, max(20, args.steps // 2), args.warmup, torch, gqa, append=append)
             if c.kv_format:
                 r["traffic"] = pmc_traffic(EXT_FP8_PMC[c.kv_format], EXT_SOURCES)
             ext.append(r)
             del c
         line["extended"] = ext
-    if args.ragged:
+    if not args.no_ragged:
         log("generating the ragged workload (8 GiB cache)")
         c = gi.ragged_decode(invalid="zero")
         r, o = bench_decode_case(c, max(10, args.steps // 4), max(3, args.warmup // 4), 1, torch, gqa)
-        us = r["call_ms_mean"] * 1e3
+        us = r["event_ms"] * 1e3
         line["ragged"] = {"workload": c.name, "bytes": r["bytes"], "flops": r["flops"],
-                          "splits": r["splits"], "us_per_call_mean": us,
+                          "splits": r["splits"], "us_per_step": us,
+                          "us_per_call_median": r["call_ms_median"] * 1e3,
                           "achieved_TBps": r["bytes"] / (us * 1e-6) / 1e12,
                           "hbm_frac": r["bytes"] / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
-                          "note": "one cache copy (8 GiB exceeds every cache level)"}
-        del o
+                          "note": "bytes count only the valid rows; one cache copy (8 GiB exceeds "
+                                  "every cache level)"}
+        del o, c
     print(json.dumps(line), flush=True)
 
 
