@@ -278,8 +278,12 @@ gqa_status gqa_prefill_ex(const void *q, const void *k, const void *v, int B, in
 uint64_t gqa_kv_cache_elems(uint64_t L, uint64_t Hkv, uint64_t d);
 
 /* Algorithmic bytes of one gqa_decode call: every valid K and V row read
- * once per KV head, plus q read and out written once.  host_seqlens is a
- * HOST array of B lengths.  Returns 0 for an unknown dtype. */
+ * once per KV head, plus q read and out written once.  The K/V part is the
+ * per-step cache traffic of "GQA reading notes", section 3 (KV cache) and
+ * its formal definition: K and V of each cached position are read once per
+ * group, not once per query head (the walkthrough of Algorithm 2 fuses the
+ * group's queries for exactly that).  host_seqlens is a HOST array of B
+ * lengths.  Returns 0 for an unknown dtype. */
 uint64_t gqa_decode_bytes(const int32_t *host_seqlens, int B, int Hq, int Hkv, int d,
                           gqa_dtype dtype);
 
@@ -289,10 +293,17 @@ uint64_t gqa_decode_bytes(const int32_t *host_seqlens, int B, int Hq, int Hkv, i
 uint64_t gqa_decode_flops(const int32_t *host_seqlens, int B, int Hq, int d);
 
 /* FLOP of one gqa_prefill call: 4 * B * Hq * d * pairs, where pairs =
- * P(P+1)/2 unmasked query-key pairs if causal, P*P otherwise. */
+ * P(P+1)/2 unmasked query-key pairs if causal, P*P otherwise.  Scores and
+ * weighted sum each take Hq * d multiply-adds per query-key pair, with no
+ * KV-head term (ttlab lesson, section "什么减少，什么不减少"); the causal mask
+ * of the prefill phase ("从MHA到GQA", the prefill/decode discussion) leaves
+ * position i its keys 0..i.  A multiply-add counts 2 FLOP. */
 uint64_t gqa_prefill_flops(int B, int P, int Hq, int d, int causal);
 
-/* Algorithmic bytes of one gqa_prefill call: q, k, v read once, out written once. */
+/* Algorithmic bytes of one gqa_prefill call: q, k, v read once, out written
+ * once.  K and V hold 2 * P * Hkv * d elements per sequence, the cache size
+ * formula of the ttlab lesson (section "什么减少，什么不减少") and of "GQA
+ * reading notes", section 3; q and out hold B * P * Hq * d each. */
 uint64_t gqa_prefill_bytes(int B, int P, int Hq, int Hkv, int d, gqa_dtype dtype);
 
 #ifdef __cplusplus
