@@ -446,25 +446,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_bf16_tiles(
 // ---------------------------------------------------------------------------
 // fp32 split kernel on the vector ALUs (fp32 inputs).
 //
-// Per tile of 64 keys: scores for every (head of the group, key) pair into
-// LDS, per-head online-softmax update, then each thread accumulates its
-// (head, head-dim) outputs over the tile.  The query is staged in LDS
-// already multiplied by scale*log2(e).
+// Per tile of 64 keys: the tile's K and V rows, fetched into registers with
+// coalesced 16-byte loads while the previous tile was being computed (rows
+// at or past the piece end are never read), are staged in LDS; scores for
+// every (head of the group, key) pair go to LDS; one wave per head updates
+// that head's online softmax (one key per lane, shuffle reductions); then
+// each thread accumulates its (head, head-dim) outputs over the tile.  The
+// query is staged in LDS already multiplied by scale*log2(e).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ seqlens, int Hq, int Hkv, int Lmax, int gsize, int S, int chunk,
     float c_log2, float* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
-    constexpr int TILE = 64;
+    constexpr int TILE = 64;   // keys per tile: one per lane in the softmax
     constexpr int MAXG = 64;
     constexpr int ACC = MAXG * D / kDecodeThreads;
+    constexpr int RP = D + 4;  // padded LDS row: rows 4 banks apart for the score reads
+    constexpr int C4 = D / 4;  // 16-byte pieces per row
+    constexpr int PER = TILE * C4 / kDecodeThreads;  // pieces per thread and operand
 
     __shared__ float sq[MAXG * D];
     __shared__ float ss[MAXG * TILE];
+    __shared__ __align__(16) float sk[TILE * RP];
+    __shared__ __align__(16) float sv[TILE * D];
     __shared__ float sm[MAXG], sl[MAXG], sa[MAXG];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     // (b, KV head) varies fastest and the piece slowest: workgroups are dealt
     // to the XCDs round-robin, so each XCD gets the same mix of pieces, and
     // every first piece (always full) is dispatched before any later one.
@@ -491,16 +501,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
     float acc[ACC];
 #pragma unroll
     for (int i = 0; i < ACC; ++i) acc[i] = 0.f;
-    __syncthreads();
 
+    f32x4 nk[PER], nv[PER];
+    auto fetch = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = tid + kDecodeThreads * p;
+            const int j = idx / C4, c = 4 * (idx % C4);
+            nk[p] = nv[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t0 + j < end) {
+                nk[p] = *reinterpret_cast<const f32x4*>(kb + (int64_t)(t0 + j) * rs + c);
+                nv[p] = *reinterpret_cast<const f32x4*>(vb + (int64_t)(t0 + j) * rs + c);
+            }
+        }
+    };
+    if (start < end) fetch(start);
     for (int t0 = start; t0 < end; t0 += TILE) {
         const int cnt = min(TILE, end - t0);
+        __syncthreads();  // the previous tile's K, V and scores have been read
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = tid + kDecodeThreads * p;
+            const int j = idx / C4, c = 4 * (idx % C4);
+            *reinterpret_cast<f32x4*>(sk + j * RP + c) = nk[p];
+            *reinterpret_cast<f32x4*>(sv + j * D + c) = nv[p];
+        }
+        __syncthreads();
+        if (t0 + TILE < end) fetch(t0 + TILE);  // in flight while this tile is computed
         for (int idx = tid; idx < gsize * TILE; idx += kDecodeThreads) {
             const int h = idx / TILE, j = idx % TILE;
             float sc = kNegInf;
             if (j < cnt) {
-                const float* kr = kb + (int64_t)(t0 + j) * rs;
                 const float* qh = sq + h * D;
+                const float* kr = sk + j * RP;
                 float dot = 0.f;
                 for (int c = 0; c < D; ++c) dot += qh[c] * kr[c];
                 sc = dot;
@@ -508,20 +541,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
             ss[h * TILE + j] = sc;
         }
         __syncthreads();
-        for (int h = tid; h < gsize; h += kDecodeThreads) {
-            float mx = kNegInf;
-            for (int j = 0; j < cnt; ++j) mx = fmaxf(mx, ss[h * TILE + j]);
-            const float mn = fmaxf(sm[h], mx);
-            const float a = fast_exp2(sm[h] - mn);
-            float sum = 0.f;
-            for (int j = 0; j < TILE; ++j) {
-                const float pj = j < cnt ? fast_exp2(ss[h * TILE + j] - mn) : 0.f;
-                ss[h * TILE + j] = pj;
-                sum += pj;
+        for (int h = wave; h < gsize; h += kDecodeWaves) {
+            const float sc = ss[h * TILE + lane];  // -inf past cnt
+            float mx = sc;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float mo = sm[h];
+            const float mn = fmaxf(mo, mx);
+            const float pj = fast_exp2(sc - mn);
+            float sum = pj;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            ss[h * TILE + lane] = pj;
+            if (lane == 0) {
+                const float a = fast_exp2(mo - mn);
+                sl[h] = sl[h] * a + sum;
+                sm[h] = mn;
+                sa[h] = a;
             }
-            sl[h] = sl[h] * a + sum;
-            sm[h] = mn;
-            sa[h] = a;
         }
         __syncthreads();
 #pragma unroll
@@ -530,12 +567,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_f32(
             if (idx < gsize * D) {
                 const int h = idx / D, c = idx % D;
                 float a = acc[i] * sa[h];
-                for (int j = 0; j < cnt; ++j) a += ss[h * TILE + j] * vb[(int64_t)(t0 + j) * rs + c];
+                for (int j = 0; j < cnt; ++j) a += ss[h * TILE + j] * sv[j * D + c];
                 acc[i] = a;
             }
         }
-        __syncthreads();
     }
+    __syncthreads();  // sm, sl are complete (also when the piece is empty)
 
 #pragma unroll
     for (int i = 0; i < ACC; ++i) {

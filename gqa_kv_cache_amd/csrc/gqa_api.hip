@@ -20,6 +20,7 @@ namespace {
 
 constexpr int kMaxGroup = 64;
 constexpr int64_t kMaxChunk = 8192;  // keys per automatic decode piece, at most
+constexpr int64_t kMinChunkF32 = 256;  // keys per automatic fp32 decode piece, at least
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -122,6 +123,9 @@ gqa_status plan_decode(int B, int Hq, int Hkv, int d, int Lmax, gqa_dtype dtype,
         if (st != GQA_OK) return st;
         const int64_t pairs = (int64_t)B * Hkv;
         int64_t splits = cdiv(cus, pairs);
+        // fp32 pieces hold at least kMinChunkF32 keys: below that the fixed
+        // cost of a piece and of the merge outweighs the parallelism
+        if (dtype == GQA_F32 && splits > cdiv(Lmax, kMinChunkF32)) splits = cdiv(Lmax, kMinChunkF32);
         if (splits < cdiv(Lmax, kMaxChunk)) splits = cdiv(Lmax, kMaxChunk);
         chunk = cdiv(cdiv(Lmax, splits), gqa::kDecodeStep) * gqa::kDecodeStep;
     } else {
