@@ -147,6 +147,20 @@ def test_four_head_tiles_long_pieces(B, Hq, Hkv, L, lens, splits):
     check_oracle(c, from_dev(run_decode(c, splits)))
 
 
+@pytest.mark.timeout(400)  # 2.1 GB of cache to draw and an fp64 oracle over half a million keys
+def test_longest_cache_the_offsets_allow():
+    """Lmax = 524,255 is the largest length the 32-bit offset check admits at
+    Hkv 8, d 128 ((Lmax + 32) * Hkv * d * 4 <= 2^31 - 1); one more is refused.
+    The automatic plan cuts it into 64 pieces of 8,192 keys."""
+    Lmax = 524255
+    with pytest.raises(gqa.GqaError):
+        gqa.decode_workspace_size(1, 64, 8, 128, Lmax + 1, gqa.BF16, 0)
+    assert gqa.decode_num_splits(1, 64, 8, 128, Lmax, gqa.BF16, 0) == 64
+    c = gi.decode_case(1, 64, 8, 128, Lmax, [Lmax], "bf16", q_seed=17, kv_seed=18, invalid="nan",
+                       name="decode_longest_B1_Hq64_Hkv8_d128_L524255")
+    check_oracle(c, from_dev(run_decode(c)))
+
+
 def test_one_key_per_split():
     c = gi.decode_case(3, 8, 2, 128, 100, [100, 57, 1], "bf16", q_seed=7, kv_seed=8, invalid="nan")
     check_oracle(c, from_dev(run_decode(c, 100)))

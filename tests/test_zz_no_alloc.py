@@ -69,3 +69,37 @@ def test_plan_above_the_scratch_is_refused():
     # the same plan within the limit runs
     want, got = _both(c, 16)
     assert np.array_equal(bits(got), bits(want))
+
+
+def test_captured_in_a_graph():
+    """The callers it is for: capture a split decode through the entry point
+    once, then replay it after eager calls (of both entry points, on the
+    same stream) and after in-place changes of q; every replay equals an
+    eager gqa_decode of the same inputs bit for bit."""
+    c = gi.decode_case(4, 32, 8, 128, 1000, [1000, 999, 3, 640], "bf16", q_seed=67, kv_seed=68,
+                       invalid="nan")
+    q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
+    sl = torch.from_numpy(c.seqlens).cuda()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gqa.decode_noalloc(q, k, v, sl, out, c.scale, num_splits=3)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqa.decode_noalloc(q, k, v, sl, out, c.scale, num_splits=3)
+    other = to_dev(gi.decode_case(4, 32, 8, 128, 1000, [1000, 999, 3, 640], "bf16", q_seed=69,
+                                  kv_seed=68).q)
+    for i in range(4):
+        src = other if i % 2 else to_dev(c.q)
+        q.copy_(src)
+        want = bits(gqa.decode(src, k, v, sl, c.scale, num_splits=3))
+        scratch_user = torch.empty_like(q)
+        gqa.decode_noalloc(other, k, v, sl, scratch_user, c.scale, num_splits=5)  # reuses the scratch
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), want), i
