@@ -60,7 +60,9 @@ def source_digest(paths) -> str:
 
 def profile_fields(summary_rel, sources):
     """Fields of a committed rocprofv3 summary, or None if it is missing or was
-    measured on other kernel sources (the summary records their digest)."""
+    measured on other kernel sources (the summary records their digest).  A
+    summary covering several workloads lists the headline one first; the
+    first value of a repeated field is kept."""
     path = os.path.join(ROOT, summary_rel)
     if not os.path.exists(path):
         return None
@@ -69,7 +71,7 @@ def profile_fields(summary_rel, sources):
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
+                vals.setdefault(k.strip(), v.strip())
     if vals.get("source_sha256") != source_digest(sources):
         return None
     return vals
@@ -371,6 +373,28 @@ def bench_prefill(steps, warmup, torch, gqa, c):
     }, out
 
 
+def bench_prefill_window(steps, warmup, torch, gqa, c, window):
+    """The causal prefill workload with a sliding window: position i attends
+    to the last `window` positions up to i.  FLOP count the visible pairs:
+    sum over i of min(i + 1, window), per sequence and query head."""
+    q, k, v = to_dev(c.q, torch), to_dev(c.k, torch), to_dev(c.v, torch)
+    out = torch.empty_like(q)
+
+    def fn(i):
+        gqa.prefill(q, k, v, causal=True, scale=c.scale, out=out, window=window)
+
+    wall_ms, ev_ms, per_call = time_calls(fn, steps, warmup, torch)
+    B, P, Hq, d = c.q.shape
+    w = min(window, P)
+    pairs = w * (w + 1) // 2 + (P - w) * w
+    flops = 4 * B * Hq * d * pairs
+    tflops = flops / (ev_ms * 1e-3) / 1e12
+    return {"workload": c.name.replace("_causal", "_window%d" % window), "window": window,
+            "flops": flops, "us_per_call_median": median(per_call) * 1e3,
+            "us_per_step_stream": ev_ms * 1e3, "achieved_TFLOPs": tflops,
+            "mfma_frac": tflops / BF16_PEAK_TFLOPS}
+
+
 def bench_tiny(steps, warmup, torch, gqa):
     """The tiny fp32 step (B1 Hq8 d64 L128) for Hkv 2 (GQA), 8 (MHA), 1 (MQA):
     launch-bound, reported for completeness."""
@@ -470,7 +494,11 @@ def main():
         if not args.no_cpu_baseline:
             log("timing the CPU oracle on the whole prefill workload")
             line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pc, pout, torch)
-        del pout, pc
+        del pout
+        log("timing prefill with a 1024-key window")
+        line["prefill"]["window"] = bench_prefill_window(max(10, args.steps // 4),
+                                                         max(3, args.warmup // 4), torch, gqa, pc, 1024)
+        del pc
     if not args.no_sweep:
         sweep = []
         for hkv in gi.SWEEP_HKV:
