@@ -22,7 +22,9 @@ import json
 import math
 import os
 import platform
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +106,61 @@ def mfma_counters(summary_rel, sources):
     return out or None
 
 
+def smi_clocks():
+    """Current clocks of GPU 0 as amd-smi reports them (MHz): the shader clock
+    of each XCD and the memory clock.  None when amd-smi is missing or fails."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=60)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    text = r.stdout
+    starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
+    if r.returncode != 0 or not starts:
+        return None
+    try:
+        data = json.loads(text[min(starts):])
+    except ValueError:
+        return None
+    if isinstance(data, dict):
+        data = data.get("gpu_data", [data])
+    clk = data[0].get("clock", {}) if data else {}
+
+    def mhz(dom):
+        v = clk.get(dom)
+        try:
+            return float(v["clk"]["value"])
+        except (TypeError, KeyError, ValueError):
+            return None
+
+    gfx = [m for m in (mhz("gfx_%d" % x) for x in range(64)) if m is not None]
+    if not gfx:
+        return None
+    return {"gfx_mhz_per_xcd": gfx, "gfx_mhz_mean": sum(gfx) / len(gfx), "mem_mhz": mhz("mem_0")}
+
+
+def clocks_under_load(fn, torch, delay_s=0.5):
+    """amd-smi's clocks taken while fn(i) calls, queued back to back, keep the
+    GPU busy: the sample is read after delay_s of sustained work."""
+    got = {}
+
+    def probe():
+        time.sleep(delay_s)
+        got["clocks"] = smi_clocks()
+
+    th = threading.Thread(target=probe)
+    th.start()
+    i = 0
+    while th.is_alive():
+        fn(i)
+        i += 1
+    th.join()
+    torch.cuda.synchronize()
+    if got.get("clocks") is not None:
+        got["clocks"]["calls_queued"] = i
+    return got.get("clocks")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -152,7 +209,7 @@ def pct(xs, p):
     return s[min(len(s) - 1, int(p / 100.0 * len(s)))]
 
 
-def bench_decode_case(case, steps, warmup, copies, torch, gqa):
+def bench_decode_case(case, steps, warmup, copies, torch, gqa, clocks=False):
     q = to_dev(case.q, torch)
     ks = [to_dev(case.k, torch)]
     vs = [to_dev(case.v, torch)]
@@ -172,11 +229,14 @@ def bench_decode_case(case, steps, warmup, copies, torch, gqa):
         gqa.decode(q, ks[i], vs[i], sl, case.scale, out=out, workspace=ws)
 
     wall_ms, ev_ms, per_call = time_calls(fn, steps, warmup, torch, rotate=copies)
+    under_load = clocks_under_load(lambda i: fn(i % copies), torch) if clocks else None
     nbytes = gqa.decode_bytes(case.seqlens, Hq, Hkv, d, dt)
     flops = gqa.decode_flops(case.seqlens, Hq, d)
     res = dict(bytes=nbytes, flops=flops, splits=splits, wall_ms=wall_ms, event_ms=ev_ms,
                call_ms_median=median(per_call), call_ms_mean=sum(per_call) / len(per_call),
                call_ms_p10=pct(per_call, 10), call_ms_p90=pct(per_call, 90))
+    if clocks:
+        res["clocks_under_load"] = under_load
     del ks, vs
     return res, out
 
@@ -346,7 +406,7 @@ def cpu_baseline_prefill(case, gpu_out, torch):
     }
 
 
-def bench_prefill(steps, warmup, torch, gqa, c):
+def bench_prefill(steps, warmup, torch, gqa, c, clocks=False):
     q, k, v = to_dev(c.q, torch), to_dev(c.k, torch), to_dev(c.v, torch)
     out = torch.empty_like(q)
 
@@ -354,12 +414,13 @@ def bench_prefill(steps, warmup, torch, gqa, c):
         gqa.prefill(q, k, v, causal=True, scale=c.scale, out=out)
 
     wall_ms, ev_ms, per_call = time_calls(fn, steps, warmup, torch)
+    under_load = clocks_under_load(fn, torch) if clocks else None
     B, P, Hq, d = c.q.shape
     Hkv = c.k.shape[2]
     flops = gqa.prefill_flops(B, P, Hq, d, True)
     mean_ms = sum(per_call) / len(per_call)
     tflops = flops / (ev_ms * 1e-3) / 1e12
-    return {
+    res = {
         "workload": c.name, "flops": flops, "bytes": gqa.prefill_bytes(B, P, Hq, Hkv, d, gqa.BF16),
         "us_per_call_median": median(per_call) * 1e3, "us_per_call_mean": mean_ms * 1e3,
         "us_per_step_stream": ev_ms * 1e3,
@@ -370,7 +431,10 @@ def bench_prefill(steps, warmup, torch, gqa, c):
                      "traffic": pmc_traffic(PREFILL_PMC, PREFILL_SOURCES),
                      "mfma_counters": mfma_counters(PREFILL_MFMA, PREFILL_SOURCES),
                      "kernel": "prefill_bf16"},
-    }, out
+    }
+    if clocks:
+        res["clocks_under_load"] = under_load
+    return res, out
 
 
 def bench_prefill_window(steps, warmup, torch, gqa, c, window):
@@ -418,6 +482,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=3, help="rotating copies of the KV cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock samples")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch (8 GiB cache)")
@@ -440,10 +505,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     gqa.load()
+    clocks = not args.no_clocks
+    idle_before = smi_clocks() if clocks else None
     log("generating the decode workload")
     case = gi.decode_70b(invalid="zero")
     log("timing decode: %d warm-up + %d steps, %d cache copies" % (args.warmup, args.steps, args.copies))
-    res, out = bench_decode_case(case, args.steps, args.warmup, args.copies, torch, gqa)
+    res, out = bench_decode_case(case, args.steps, args.warmup, args.copies, torch, gqa, clocks=clocks)
     torch.cuda.synchronize()
     ms = res["event_ms"]  # average duration per step over the timed region (stream events)
     value = res["bytes"] / (ms * 1e-3) / 1e12
@@ -490,7 +557,7 @@ def main():
         log("timing prefill")
         pc = gi.prefill_causal()
         line["prefill"], pout = bench_prefill(max(10, args.steps // 4), max(3, args.warmup // 4),
-                                              torch, gqa, pc)
+                                              torch, gqa, pc, clocks=clocks)
         if not args.no_cpu_baseline:
             log("timing the CPU oracle on the whole prefill workload")
             line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pc, pout, torch)
@@ -559,6 +626,13 @@ def main():
                           "note": "bytes count only the valid rows; one cache copy (8 GiB exceeds "
                                   "every cache level)"}
         del o, c
+    if clocks:
+        line["clocks"] = {
+            "source": "amd-smi metric --clock, current clocks in MHz (shader clock per XCD, memory)",
+            "idle_before": idle_before,
+            "under_decode": res.get("clocks_under_load"),
+            "under_prefill": line.get("prefill", {}).pop("clocks_under_load", None),
+            "idle_after": smi_clocks()}
     print(json.dumps(line), flush=True)
 
 

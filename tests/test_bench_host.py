@@ -2,6 +2,7 @@
 the committed rocprofv3 summaries, and that those summaries were taken on
 the kernel sources now in the tree (otherwise bench.py reports null for
 their figures)."""
+import json
 import os
 import subprocess
 import sys
@@ -65,3 +66,17 @@ def test_committed_counters_read_back():
     m = bench.mfma_counters(bench.PREFILL_MFMA, bench.PREFILL_SOURCES)
     assert m["algorithmic_flop_per_launch"] == 274945015808
     assert 0.0 < m["mfma_busy_frac"] < 1.0 and 1.0 < m["shader_clock_ghz"] < 2.5
+
+
+def test_clock_reader_parses_the_amd_smi_layout(monkeypatch):
+    body = {"gpu_data": [{"gpu": 0, "clock": dict(
+        {"gfx_%d" % x: {"clk": {"value": 2000 + x, "unit": "MHz"}, "max_clk": {"value": 2400, "unit": "MHz"}}
+         for x in range(8)},
+        mem_0={"clk": {"value": 2000, "unit": "MHz"}}, fclk_0="N/A")}]}
+    out = "WARNING: some notice\n" + json.dumps(body)
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: subprocess.CompletedProcess(a, 0, out, ""))
+    c = bench.smi_clocks()
+    assert c["gfx_mhz_per_xcd"] == [2000.0 + x for x in range(8)]
+    assert c["gfx_mhz_mean"] == 2003.5 and c["mem_mhz"] == 2000.0
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: subprocess.CompletedProcess(a, 1, "", "no GPU"))
+    assert bench.smi_clocks() is None
