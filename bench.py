@@ -148,7 +148,7 @@ def clocks_under_load(fn, torch, delay_s=0.5):
         time.sleep(delay_s)
         got["clocks"] = smi_clocks()
 
-    th = threading.Thread(target=probe)
+    th = threading.Thread(target=probe, daemon=True)
     th.start()
     i = 0
     while th.is_alive():
