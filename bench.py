@@ -139,26 +139,35 @@ def smi_clocks():
     return {"gfx_mhz_per_xcd": gfx, "gfx_mhz_mean": sum(gfx) / len(gfx), "mem_mhz": mhz("mem_0")}
 
 
-def clocks_under_load(fn, torch, delay_s=0.5):
-    """amd-smi's clocks taken while fn(i) calls, queued back to back, keep the
-    GPU busy: the sample is read after delay_s of sustained work."""
-    got = {}
+def clocks_under_load(fn, torch, delay_s=1.0, samples=3):
+    """amd-smi's clocks read while fn(i) calls, queued back to back, keep the
+    GPU busy: `samples` readings in a row, the first after delay_s of
+    sustained work (amd-smi's figures trail the load, so the last reading is
+    the one to take)."""
+    got = []
 
     def probe():
         time.sleep(delay_s)
-        got["clocks"] = smi_clocks()
+        for _ in range(samples):
+            got.append(smi_clocks())
 
     th = threading.Thread(target=probe, daemon=True)
     th.start()
     i = 0
+    t0 = time.time()
     while th.is_alive():
         fn(i)
         i += 1
     th.join()
     torch.cuda.synchronize()
-    if got.get("clocks") is not None:
-        got["clocks"]["calls_queued"] = i
-    return got.get("clocks")
+    got = [g for g in got if g is not None]
+    if not got:
+        return None
+    last = dict(got[-1])
+    last["gfx_mhz_mean_per_reading"] = [g["gfx_mhz_mean"] for g in got]
+    last["calls_queued"] = i
+    last["seconds_of_load"] = time.time() - t0
+    return last
 
 
 def log(msg):
