@@ -89,6 +89,20 @@ def test_ragged_full():
     check_oracle(c, got)
 
 
+# --- many short sequences: one small workgroup each, some with no rows ------
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,d", [("bf16", 1024, 32, 8, 128), ("f32", 512, 8, 2, 64)])
+@pytest.mark.parametrize("splits", [0, 2, 3])
+def test_many_short_sequences(dtype, B, Hq, Hkv, d, splits):
+    lens = np.random.default_rng(61).integers(0, 41, B).astype(np.int32)
+    lens[:3] = (0, 40, 1)
+    c = gi.decode_case(B, Hq, Hkv, d, 40, lens, dtype, q_seed=62, kv_seed=63, invalid="nan",
+                       name="many_short_%s" % dtype)
+    got = from_dev(run_decode(c, splits))
+    check_oracle(c, got)
+    assert not np.any(got.reshape(B, -1)[lens == 0])   # no visible row: zero output
+
+
 # --- randomised shapes: head dims, group sizes, lengths, ragged, splits ------
 
 SEQ = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
