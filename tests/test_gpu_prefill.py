@@ -146,6 +146,16 @@ def test_window_prefill_small(shape, window):
     check_causal("window_%d" % window, p, from_dev(out), window=window)
 
 
+@pytest.mark.parametrize("window", [0, 40])
+def test_prefill_many_sequences(window):
+    """Twelve prompts, groups of three heads (one head per workgroup): the
+    workgroup-to-(sequence, head set, row block) mapping away from B = 1, 2."""
+    p = gi.prefill_case(12, 90, 12, 4, 128, "bf16", seed=90 + window)
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=window)
+    torch.cuda.synchronize()
+    check_causal("many_sequences_%d" % window, p, from_dev(out), window=window)
+
+
 @pytest.mark.timeout(400)  # the fp64 oracle of every row takes about a minute
 def test_window_prefill_full_size_every_row():
     p = gi.prefill_case(2, 4096, 32, 8, 128, "bf16", seed=5)
