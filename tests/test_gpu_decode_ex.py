@@ -213,6 +213,24 @@ def test_append_rows_across_piece_boundaries(kv, paged, block_size):
         check_oracle(c, from_dev(out))
 
 
+@pytest.mark.parametrize("kv,paged,window", [("same", False, 0), ("fp8", True, 0), ("same", True, 20),
+                                             ("e5m2", False, 20)])
+def test_many_short_sequences_with_append(kv, paged, window):
+    """256 sequences of 2-50 rows, two new tokens each stored in the same
+    launch: small workgroups, pages of 16 rows, short windows."""
+    lens = np.random.default_rng(57).integers(2, 51, 256)
+    lens[:2] = (2, 50)
+    c = case(B=256, T=2, Hq=16, Hkv=4, Lmax=64, seqlens=lens, kv=kv, paged=paged, block_size=16,
+             window=window, seed=58)
+    out, k, v = run_ex(c, append=True)
+    want_k, want_v = c.k_pre.copy(), c.v_pre.copy()
+    orc.append(want_k, want_v, c.k_new, c.v_new, c.seqlens, block_table=c.block_table,
+               block_size=c.block_size)
+    assert np.array_equal(k.view(torch.uint8).cpu().numpy().reshape(-1), want_k.view(np.uint8).reshape(-1))
+    assert np.array_equal(v.view(torch.uint8).cpu().numpy().reshape(-1), want_v.view(np.uint8).reshape(-1))
+    check_oracle(c, from_dev(out))
+
+
 def test_without_append_reads_the_cache():
     c = case(T=2, seed=48)
     out, _, _ = run_ex(c, append=False)
