@@ -103,6 +103,30 @@ def test_many_short_sequences(dtype, B, Hq, Hkv, d, splits):
     assert not np.any(got.reshape(B, -1)[lens == 0])   # no visible row: zero output
 
 
+# --- seeded fuzz over group size, head dim, dtype, lengths and pieces -------
+
+def _fuzz_cases(n=32, seed=64):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        G = int(rng.integers(1, 65))
+        Hkv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 7))
+        Lmax = int(rng.integers(1, 1201))
+        lens = rng.integers(0, Lmax + 1, B).astype(np.int32)
+        lens[0] = Lmax
+        splits = int(rng.choice([0, 0, 1, 2, 3, 5, 9]))
+        yield i, dtype, G, Hkv, d, Lmax, tuple(int(x) for x in lens), min(splits, Lmax)
+
+
+@pytest.mark.parametrize("i,dtype,G,Hkv,d,Lmax,lens,splits", list(_fuzz_cases()))
+def test_fuzz(i, dtype, G, Hkv, d, Lmax, lens, splits):
+    c = gi.decode_case(len(lens), G * Hkv, Hkv, d, Lmax, list(lens), dtype, q_seed=100 + i,
+                       kv_seed=200 + i, invalid="nan", name="fuzz%d" % i)
+    check_oracle(c, from_dev(run_decode(c, splits)))
+
+
 # --- randomised shapes: head dims, group sizes, lengths, ragged, splits ------
 
 SEQ = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300]

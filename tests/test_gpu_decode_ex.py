@@ -231,6 +231,38 @@ def test_many_short_sequences_with_append(kv, paged, window):
     check_oracle(c, from_dev(out))
 
 
+def _ex_fuzz_cases(n=24, seed=65):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        T = int(rng.choice([1, 1, 2, 3, 4, 8]))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 64 // T + 1))                 # T * G rows per KV head, at most 64
+        d = int(rng.choice([64, 128]))
+        kv = str(rng.choice(["same", "same", "fp8", "e5m2"]))
+        paged = bool(rng.integers(0, 2))
+        bs = int(rng.choice([16, 32, 48, 64]))
+        Lmax = -(-int(rng.integers(T, 700)) // bs) * bs if paged else int(rng.integers(T, 700))
+        B = int(rng.integers(1, 6))
+        lens = rng.integers(T, Lmax + 1, B)
+        lens[0] = Lmax
+        window = int(rng.choice([0, 0, 1, 17, 64, 300]))
+        splits = int(rng.choice([0, 0, 1, 2, 5]))
+        yield i, T, G, Hkv, d, kv, paged, bs, Lmax, tuple(int(x) for x in lens), window, min(splits, Lmax)
+
+
+@pytest.mark.parametrize("i,T,G,Hkv,d,kv,paged,bs,Lmax,lens,window,splits", list(_ex_fuzz_cases()))
+def test_fuzz_ex(i, T, G, Hkv, d, kv, paged, bs, Lmax, lens, window, splits):
+    c = case(B=len(lens), T=T, Hq=G * Hkv, Hkv=Hkv, d=d, Lmax=Lmax, seqlens=lens, kv=kv, paged=paged,
+             block_size=bs, window=window, seed=300 + i)
+    out, k, v = run_ex(c, append=True, num_splits=splits)
+    want_k, want_v = c.k_pre.copy(), c.v_pre.copy()
+    orc.append(want_k, want_v, c.k_new, c.v_new, c.seqlens, block_table=c.block_table,
+               block_size=c.block_size)
+    assert np.array_equal(k.view(torch.uint8).cpu().numpy().reshape(-1), want_k.view(np.uint8).reshape(-1))
+    assert np.array_equal(v.view(torch.uint8).cpu().numpy().reshape(-1), want_v.view(np.uint8).reshape(-1))
+    check_oracle(c, from_dev(out))
+
+
 def test_without_append_reads_the_cache():
     c = case(T=2, seed=48)
     out, _, _ = run_ex(c, append=False)

@@ -156,6 +156,26 @@ def test_prefill_many_sequences(window):
     check_causal("many_sequences_%d" % window, p, from_dev(out), window=window)
 
 
+def _prefill_fuzz_cases(n=20, seed=66):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        Hkv = int(rng.integers(1, 5))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 16]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 4))
+        P = int(rng.integers(1, 400))
+        window = int(rng.choice([0, 0, 0, 1, 31, 33, 100]))
+        yield i, B, P, G * Hkv, Hkv, d, window
+
+
+@pytest.mark.parametrize("i,B,P,Hq,Hkv,d,window", list(_prefill_fuzz_cases()))
+def test_fuzz_prefill(i, B, P, Hq, Hkv, d, window):
+    p = gi.prefill_case(B, P, Hq, Hkv, d, "bf16", seed=400 + i)
+    out = gqa.prefill(to_dev(p.q), to_dev(p.k), to_dev(p.v), True, p.scale, window=window)
+    torch.cuda.synchronize()
+    check_causal("fuzz%d" % i, p, from_dev(out), window=window)
+
+
 @pytest.mark.timeout(400)  # the fp64 oracle of every row takes about a minute
 def test_window_prefill_full_size_every_row():
     p = gi.prefill_case(2, 4096, 32, 8, 128, "bf16", seed=5)
