@@ -8,8 +8,10 @@ a call fails, an exception is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import enum
+import functools
 import math
 import os
 
@@ -134,6 +136,31 @@ def _require_cuda(name, t):
         raise ValueError("gqa: %s must be contiguous" % name)
 
 
+def _on_device(index):
+    """The device context a call needs: none when `index` is already current
+    (the library plans and launches on the current device)."""
+    import torch
+    if index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(index)
+
+
+def _stream(index):
+    """Raw handle of the current stream of device `index`."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+@functools.lru_cache(maxsize=256)
+def _decode_ws_bytes(B, Hq, Hkv, d, Lmax, dtype_code, num_splits, device_index):
+    """decode_workspace_size per device (the automatic plan depends on the
+    device's compute-unit count); called with that device current."""
+    return decode_workspace_size(B, Hq, Hkv, d, Lmax, dtype_code, num_splits)
+
+
 def decode_num_splits(B, Hq, Hkv, d, Lmax, dtype_code, num_splits=0) -> int:
     out = ctypes.c_int(0)
     _check(load().gqa_decode_num_splits(B, Hq, Hkv, d, Lmax, dtype_code, num_splits,
@@ -185,15 +212,16 @@ def decode(q, k_cache, v_cache, seqlens, scale=None, out=None, num_splits=0, wor
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    with torch.cuda.device(q.device):
-        need = decode_workspace_size(B, Hq, Hkv, d, Lmax, dt, num_splits)
+    idx = q.device.index
+    with _on_device(idx):
+        need = _decode_ws_bytes(B, Hq, Hkv, d, Lmax, dt, int(num_splits), idx)
         ws_ptr, ws_bytes = None, 0
         if need:
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             _require_cuda("workspace", workspace)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+        stream = _stream(idx)
         st = lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                             B, Hq, Hkv, d, Lmax, float(scale), dt, out.data_ptr(), ws_ptr, ws_bytes,
                             int(num_splits), stream)
@@ -213,8 +241,8 @@ def decode_noalloc(q, k_cache, v_cache, seqlens, out, scale=None, num_splits=0):
         raise ValueError("gqa: decode_noalloc writes into a caller-provided out")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with _on_device(q.device.index):
+        stream = _stream(q.device.index)
         st = lib.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                     seqlens.data_ptr(), B, Hq, Hkv, d, Lmax, float(scale), dt,
                                     out.data_ptr(), int(num_splits), stream)
@@ -320,7 +348,7 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
     a.scale, a.dtype, a.kv_dtype = float(scale), BF16, kv
     a.block_size, a.max_blocks, a.num_blocks = int(block_size), max_blocks, num_blocks
     a.window, a.out, a.num_splits = int(window), out.data_ptr(), int(num_splits)
-    with torch.cuda.device(q.device):
+    with _on_device(q.device.index):
         need = ctypes.c_size_t(0)
         _check(lib.gqa_decode_ex_workspace_size(ctypes.byref(a), ctypes.byref(need)),
                "gqa_decode_ex_workspace_size")
@@ -329,7 +357,7 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
                 workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
             _require_cuda("workspace", workspace)
             a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+        stream = _stream(q.device.index)
         st = lib.gqa_decode_ex(ctypes.byref(a), stream)
     _check(st, "gqa_decode_ex")
     return out
@@ -361,8 +389,8 @@ def prefill(q, k, v, causal=True, scale=None, out=None, window=0):
         _require_cuda("out", out)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("gqa: out must match q in shape and dtype")
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with _on_device(q.device.index):
+        stream = _stream(q.device.index)
         st = lib.gqa_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, P, Hq, Hkv, d,
                                 1 if causal else 0, int(window), float(scale), dt, out.data_ptr(),
                                 stream)
