@@ -154,6 +154,9 @@ def _stream(index):
     return torch.cuda.current_stream(index).cuda_stream
 
 
+_EX_WS_BYTES = {}   # gqa_decode_ex workspace bytes by plan inputs and device
+
+
 @functools.lru_cache(maxsize=256)
 def _decode_ws_bytes(B, Hq, Hkv, d, Lmax, dtype_code, num_splits, device_index):
     """decode_workspace_size per device (the automatic plan depends on the
@@ -348,13 +351,22 @@ def decode_ex(q, k_cache, v_cache, seqlens, *, scale=None, k_scale=None, v_scale
     a.scale, a.dtype, a.kv_dtype = float(scale), BF16, kv
     a.block_size, a.max_blocks, a.num_blocks = int(block_size), max_blocks, num_blocks
     a.window, a.out, a.num_splits = int(window), out.data_ptr(), int(num_splits)
-    with _on_device(q.device.index):
-        need = ctypes.c_size_t(0)
-        _check(lib.gqa_decode_ex_workspace_size(ctypes.byref(a), ctypes.byref(need)),
-               "gqa_decode_ex_workspace_size")
-        if need.value:
+    idx = q.device.index
+    with _on_device(idx):
+        # the plan reads only these fields (and the device's compute units)
+        key = (B, T, Hq, Hkv, d, Lmax, kv, a.block_table is not None, a.block_size, a.max_blocks,
+               a.num_blocks, a.window, a.num_splits, idx)
+        need = _EX_WS_BYTES.get(key)
+        if need is None:
+            n = ctypes.c_size_t(0)
+            _check(lib.gqa_decode_ex_workspace_size(ctypes.byref(a), ctypes.byref(n)),
+                   "gqa_decode_ex_workspace_size")
+            need = n.value
+            if len(_EX_WS_BYTES) < 1024:
+                _EX_WS_BYTES[key] = need
+        if need:
             if workspace is None:
-                workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             _require_cuda("workspace", workspace)
             a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         stream = _stream(q.device.index)
